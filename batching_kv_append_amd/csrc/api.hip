@@ -1,0 +1,331 @@
+// C-ABI entry points of libkvc.so: argument validation, workspace layout and
+// the launch sequence of one ragged paged-attention step.
+//
+// Every check that can fail happens before the first launch, so a call that
+// returns an error has enqueued nothing.  Values inside device arrays are not
+// read here (that would need a device-to-host copy and a sync on every call);
+// the kernels guard every table lookup instead, and KVC_DEBUG=1 adds a
+// synchronous host-side check of the lengths and the table.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kvc.h"
+#include "kvc_launch.h"
+#include "kvc_status.h"
+
+namespace kvc {
+
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cache[dev] = n;
+    return n;
+}
+
+}  // namespace kvc
+
+namespace {
+
+using kvc::WsLayout;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool debug_mode() {
+    const char* e = std::getenv("KVC_DEBUG");
+    return e && e[0] && e[0] != '0';
+}
+
+int check_shape(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                const char* fn) {
+    char msg[256];
+    if (num_kv_heads <= 0 || num_q_heads <= 0) {
+        std::snprintf(msg, sizeof msg, "%s: head counts must be positive", fn);
+        return kvc_fail(KVC_ERR_INVALID_ARG, msg);
+    }
+    if (num_q_heads % num_kv_heads != 0) {
+        std::snprintf(msg, sizeof msg, "%s: num_q_heads %% num_kv_heads != 0", fn);
+        return kvc_fail(KVC_ERR_INVALID_ARG, msg);
+    }
+    const int G = num_q_heads / num_kv_heads;
+    if (!(G == 1 || G == 2 || G % 4 == 0)) {
+        std::snprintf(msg, sizeof msg, "%s: head ratio %d unsupported (1, 2 or a multiple of 4)", fn, G);
+        return kvc_fail(KVC_ERR_UNSUPPORTED, msg);
+    }
+    if (head_dim != 16 && head_dim != 128) {
+        std::snprintf(msg, sizeof msg, "%s: head_dim %d unsupported (16 or 128)", fn, head_dim);
+        return kvc_fail(KVC_ERR_UNSUPPORTED, msg);
+    }
+    if (block_size != 4 && block_size != 16) {
+        std::snprintf(msg, sizeof msg, "%s: block_size %d unsupported (4 or 16)", fn, block_size);
+        return kvc_fail(KVC_ERR_UNSUPPORTED, msg);
+    }
+    return KVC_OK;
+}
+
+int check_kv_shape(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, const char* fn) {
+    return check_shape(num_kv_heads, num_kv_heads, head_dim, block_size, fn);
+}
+
+int hip_fail(hipError_t e, const char* fn) {
+    char msg[256];
+    std::snprintf(msg, sizeof msg, "%s: %s", fn, hipGetErrorString(e));
+    return kvc_fail(KVC_ERR_HIP, msg);
+}
+
+// KVC_DEBUG=1: copy lengths and table back and check them on the host.
+int debug_check(const int32_t* cu_d, const int32_t* ctx_d, const int32_t* table_d, int32_t num_seqs,
+                int32_t total_q, int32_t max_q_len, int32_t max_context_len, int32_t max_blocks,
+                int64_t num_blocks, int32_t block_size, bool after_append_only, hipStream_t st) {
+    std::vector<int32_t> cu(num_seqs + 1), ctx(num_seqs), tab((size_t)num_seqs * max_blocks);
+    hipError_t e = hipMemcpyAsync(cu.data(), cu_d, cu.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(ctx.data(), ctx_d, ctx.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(tab.data(), table_d, tab.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "KVC_DEBUG check");
+    if (cu[0] != 0 || cu[num_seqs] != total_q)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: cu_seqlens_q must start at 0 and end at total_q");
+    for (int s = 0; s < num_seqs; ++s) {
+        const int64_t q = (int64_t)cu[s + 1] - cu[s];
+        if (q < 0) return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: cu_seqlens_q decreases");
+        if (ctx[s] < 0) return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: negative context length");
+        if (!after_append_only && (q > max_q_len || ctx[s] > max_context_len))
+            return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: a length exceeds max_q_len / max_context_len");
+        const int64_t L = ctx[s] + q;
+        const int64_t nb = (L + block_size - 1) / block_size;
+        if (nb > max_blocks) return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: table row too short");
+        for (int64_t b = 0; b < nb; ++b) {
+            const int32_t id = tab[(size_t)s * max_blocks + b];
+            if (id < 0 || id >= num_blocks)
+                return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: block id out of range");
+        }
+    }
+    return KVC_OK;
+}
+
+// Optional per-kernel timing: HIP events recorded around each launch of
+// kvc_paged_attention_varlen on the caller's stream (kvc_profile_begin/end).
+struct Profiler {
+    bool on = false;
+    int32_t max_calls = 0, calls = 0;
+    std::vector<hipEvent_t> ev;  // (KVC_PROF_PHASES + 1) per call
+};
+Profiler g_prof;
+
+void prof_mark(int phase, hipStream_t st) {
+    if (!g_prof.on || g_prof.calls >= g_prof.max_calls) return;
+    hipEventRecord(g_prof.ev[(size_t)g_prof.calls * (KVC_PROF_PHASES + 1) + phase], st);
+}
+
+}  // namespace
+
+extern "C" int kvc_profile_begin(int32_t max_calls) {
+    if (max_calls < 1 || max_calls > 100000)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_profile_begin: max_calls out of range");
+    for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+    g_prof = Profiler{};
+    g_prof.ev.resize((size_t)max_calls * (KVC_PROF_PHASES + 1));
+    for (auto& e : g_prof.ev) {
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) return hip_fail(r, "kvc_profile_begin");
+    }
+    g_prof.max_calls = max_calls;
+    g_prof.on = true;
+    return KVC_OK;
+}
+
+extern "C" int kvc_profile_end(double* ms_sum, int32_t* calls) {
+    if (!ms_sum || !calls) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_profile_end: NULL pointer");
+    for (int p = 0; p < KVC_PROF_PHASES; ++p) ms_sum[p] = 0.0;
+    *calls = 0;
+    if (!g_prof.ev.empty()) {
+        for (int32_t c = 0; c < g_prof.calls; ++c) {
+            hipEvent_t* e = &g_prof.ev[(size_t)c * (KVC_PROF_PHASES + 1)];
+            hipError_t r = hipEventSynchronize(e[KVC_PROF_PHASES]);
+            if (r != hipSuccess) return hip_fail(r, "kvc_profile_end");
+            for (int p = 0; p < KVC_PROF_PHASES; ++p) {
+                float ms = 0.f;
+                r = hipEventElapsedTime(&ms, e[p], e[p + 1]);
+                if (r != hipSuccess) return hip_fail(r, "kvc_profile_end");
+                ms_sum[p] += ms;
+            }
+        }
+        *calls = g_prof.calls;
+    }
+    for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+    g_prof = Profiler{};
+    return KVC_OK;
+}
+
+extern "C" int kvc_append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             int64_t num_blocks, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t total_q,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             void* stream) {
+    const char* fn = "kvc_append_kv";
+    if (num_seqs < 0 || total_q < 0) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_append_kv: negative size");
+    if (int rc = check_kv_shape(num_kv_heads, head_dim, block_size, fn)) return rc;
+    if (num_seqs == 0 || total_q == 0) return KVC_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !context_lens)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_append_kv: NULL pointer");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_append_kv: K/V pointers must be 16-byte aligned");
+    if (num_blocks < 1 || max_blocks_per_seq < 1)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_append_kv: num_blocks and max_blocks_per_seq must be >= 1");
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_mode()) {
+        if (int rc = debug_check(cu_seqlens_q, context_lens, block_table, num_seqs, total_q, 0, 0,
+                                 max_blocks_per_seq, num_blocks, block_size, true, st))
+            return rc;
+    }
+    hipError_t e = kvc::launch_append(k_new, v_new, k_cache, v_cache, num_blocks, block_table,
+                                      max_blocks_per_seq, cu_seqlens_q, context_lens, num_seqs,
+                                      total_q, num_kv_heads, head_dim, block_size, nullptr, st);
+    return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
+}
+
+extern "C" int kvc_gather_kv(const void* k_cache, const void* v_cache, int64_t num_blocks,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, const int64_t* cu_seq_lens,
+                             int64_t total_tokens, void* k_out, void* v_out, int32_t num_seqs,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             void* stream) {
+    const char* fn = "kvc_gather_kv";
+    if (num_seqs < 0 || total_tokens < 0) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_gather_kv: negative size");
+    if (int rc = check_kv_shape(num_kv_heads, head_dim, block_size, fn)) return rc;
+    if (num_seqs == 0 || total_tokens == 0) return KVC_OK;
+    if (!k_cache || !v_cache || !block_table || !seq_lens || !cu_seq_lens || !k_out || !v_out)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_gather_kv: NULL pointer");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_out) || !aligned16(v_out))
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_gather_kv: K/V pointers must be 16-byte aligned");
+    if (num_blocks < 1 || max_blocks_per_seq < 1)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_gather_kv: num_blocks and max_blocks_per_seq must be >= 1");
+    if (total_tokens > ((int64_t)1 << 40))
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_gather_kv: total_tokens too large");
+    hipError_t e = kvc::launch_gather(k_cache, v_cache, num_blocks, block_table, max_blocks_per_seq,
+                                      seq_lens, cu_seq_lens, total_tokens, k_out, v_out, num_seqs,
+                                      num_kv_heads, head_dim, block_size, (hipStream_t)stream);
+    return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
+}
+
+extern "C" size_t kvc_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                     int32_t max_context_len, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+    if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0) return 0;
+    if (check_shape(num_q_heads, num_kv_heads, head_dim, block_size, "kvc_workspace_size") != KVC_OK)
+        return 0;
+    return kvc::ws_layout(num_seqs, total_q, max_context_len, num_q_heads, num_kv_heads, head_dim).total;
+}
+
+extern "C" int kvc_paged_attention_varlen(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+    const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs, int32_t total_q,
+    int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    const char* fn = "kvc_paged_attention_varlen";
+    if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: negative size");
+    if (int rc = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, fn)) return rc;
+    if (!std::isfinite(scale))
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: scale must be finite");
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: k_new and v_new must both be set or both NULL");
+    if (num_seqs == 0 || total_q == 0) return KVC_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !context_lens)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: NULL pointer");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (k_new && (!aligned16(k_new) || !aligned16(v_new))))
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: tensors must be 16-byte aligned");
+    if (num_blocks < 1 || max_blocks_per_seq < 1)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: num_blocks and max_blocks_per_seq must be >= 1");
+    if (max_q_len > total_q)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: max_q_len > total_q");
+    if ((int64_t)max_context_len + max_q_len > INT32_MAX / 2)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: lengths too large");
+    const WsLayout lay = kvc::ws_layout(num_seqs, total_q, max_context_len, num_q_heads,
+                                        num_kv_heads, head_dim);
+    if (lay.cap_dec > INT32_MAX / 64 || lay.cap_pre > INT32_MAX / 64)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: step too large");
+    if (!workspace || workspace_bytes < lay.total) {
+        char msg[256];
+        std::snprintf(msg, sizeof msg, "%s: workspace of %zu bytes needed, %zu given", fn,
+                      lay.total, workspace ? workspace_bytes : (size_t)0);
+        return kvc_fail(KVC_ERR_WORKSPACE, msg);
+    }
+    if (((uintptr_t)workspace & 255u) != 0)
+        return kvc_fail(KVC_ERR_WORKSPACE, "kvc_paged_attention_varlen: workspace must be 256-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_mode()) {
+        if (int rc = debug_check(cu_seqlens_q, context_lens, block_table, num_seqs, total_q,
+                                 max_q_len, max_context_len, max_blocks_per_seq, num_blocks,
+                                 block_size, false, st))
+            return rc;
+    }
+
+    kvc::StepArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.num_blocks = num_blocks;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.cu_seqlens_q = cu_seqlens_q;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.total_q = total_q;
+    a.max_q_len = max_q_len;
+    a.max_context_len = max_context_len;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.scale = scale;
+    a.ws = (char*)workspace;
+    a.lay = lay;
+    a.stream = st;
+
+    prof_mark(KVC_PROF_PLAN, st);
+    hipError_t e = kvc::launch_plan(a);
+    prof_mark(KVC_PROF_APPEND, st);
+    if (e == hipSuccess && k_new)
+        e = kvc::launch_append(k_new, v_new, k_cache, v_cache, num_blocks, block_table,
+                               max_blocks_per_seq, cu_seqlens_q, context_lens, num_seqs, total_q,
+                               num_kv_heads, head_dim, block_size,
+                               (int32_t*)((char*)workspace + lay.hdr), st);
+    prof_mark(KVC_PROF_PREFILL, st);
+    if (e == hipSuccess) e = kvc::launch_prefill(a);
+    prof_mark(KVC_PROF_DECODE, st);
+    if (e == hipSuccess) e = kvc::launch_decode(a);
+    prof_mark(KVC_PROF_MERGE, st);
+    if (e == hipSuccess) e = kvc::launch_merge(a);
+    prof_mark(KVC_PROF_PHASES, st);
+    if (g_prof.on && g_prof.calls < g_prof.max_calls) ++g_prof.calls;
+    return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
+}
+
+extern "C" int kvc_workspace_flags(const void* workspace, void* stream, int32_t* flags) {
+    if (!workspace || !flags) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_workspace_flags: NULL pointer");
+    hipStream_t st = (hipStream_t)stream;
+    int32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, (const char*)workspace + kvc::HDR_FLAGS * 4, 4,
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "kvc_workspace_flags");
+    *flags = v;
+    return KVC_OK;
+}

@@ -1,0 +1,120 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 bit handling,
+// 16-lane DPP row reductions, MFMA operand types and the workspace layout.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// ---------------------------------------------------------------------------
+// Workspace layout (caller-owned scratch of kvc_paged_attention_varlen).
+// ---------------------------------------------------------------------------
+enum HeaderSlot : int {
+    HDR_N_DEC = 0,       // decode work items (sequence, partition)
+    HDR_N_PRE = 1,       // prefill work items (sequence, position tile)
+    HDR_DEC_NEXT = 2,    // next decode unit to claim (persistent kernel)
+    HDR_N_MERGE = 3,     // decode sequences split into >1 partition
+    HDR_FLAGS = 4,       // error flags (kvc_workspace_flags)
+    HDR_WORDS = 64
+};
+enum Flag : int {
+    FLAG_TABLE_SHORT = 1,
+    FLAG_BAD_BLOCK = 2,
+    FLAG_CAPACITY = 4,
+    FLAG_CU_SEQLENS = 8
+};
+
+// Decode partition length in tokens.  Fixed (never chosen per batch), so a
+// sequence's partial sums depend only on its own logical positions and the
+// output does not change with batch composition.
+constexpr int DECODE_PART = 256;
+
+// Prefill: each wave owns one query head and QW consecutive positions; a
+// workgroup of 4 waves covers HPW heads x (4/HPW) position blocks.
+constexpr int PREFILL_QW = 64;
+constexpr int PREFILL_TK = 64;  // keys per LDS tile
+
+struct WsLayout {
+    size_t hdr, dec_base, dec_items, pre_items, merge_list, ml, acc, total;
+    int64_t cap_dec, cap_pre;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Prefill heads per workgroup for a group ratio G (G <= 4 divides 4, or G % 4 == 0).
+inline int prefill_hpw(int G) { return G >= 4 ? 4 : G; }
+inline int prefill_span(int G) { return PREFILL_QW * (4 / prefill_hpw(G)); }
+
+inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context_len,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+    WsLayout w{};
+    const int G = num_q_heads / num_kv_heads;
+    const int64_t parts = ((int64_t)max_context_len + 1 + DECODE_PART - 1) / DECODE_PART;
+    w.cap_dec = (int64_t)num_seqs * parts;
+    w.cap_pre = (int64_t)total_q / prefill_span(G) + num_seqs;
+    size_t off = 0;
+    w.hdr = off;        off = align_up(off + HDR_WORDS * 4, 256);
+    w.dec_base = off;   off = align_up(off + (size_t)num_seqs * 4, 256);
+    w.dec_items = off;  off = align_up(off + (size_t)w.cap_dec * 8, 256);
+    w.pre_items = off;  off = align_up(off + (size_t)w.cap_pre * 8, 256);
+    w.merge_list = off; off = align_up(off + (size_t)num_seqs * 4, 256);
+    w.ml = off;         off = align_up(off + (size_t)w.cap_dec * num_q_heads * 2 * 4, 256);
+    w.acc = off;        off = align_up(off + (size_t)w.cap_dec * num_q_heads * head_dim * 4, 256);
+    w.total = off;
+    return w;
+}
+
+#ifdef __HIPCC__
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  Storage is raw uint16; widening is exact (bf16 is the top
+// half of an fp32).  Narrowing uses the compiler's __bf16 conversion, which is
+// round-to-nearest-even and lowers to v_cvt_pk_bf16_f32 on gfx950.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Sum over groups of LANES consecutive lanes (LANES in {2, 4, 8, 16}) with DPP
+// row operations; every lane of a group ends with the group's sum.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16, "group size");
+    // quad_perm [1,0,3,2]: swap neighbours
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+    if constexpr (LANES >= 4)  // quad_perm [2,3,0,1]: swap pairs
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+    if constexpr (LANES >= 8)  // row_half_mirror: lane i <-> 7-i, joins the two quads
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+    if constexpr (LANES >= 16)  // row_mirror: lane i <-> 15-i, joins the two halves
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+    return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) {
+    return __shfl_xor(x, mask, 64);
+}
+
+__device__ __forceinline__ void set_flag(int32_t* hdr, int flag) {
+    atomicOr(hdr + HDR_FLAGS, flag);
+}
+
+// Index of the sequence that owns row t: the largest s with cu[s] <= t.
+template <typename T>
+__device__ __forceinline__ int find_seq(const T* cu, int num_seqs, int64_t t) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+#endif  // __HIPCC__
+
+}  // namespace kvc

@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (one translation unit each).
+// Arguments are validated by the C-ABI layer before any of these run.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc_device.h"
+
+namespace kvc {
+
+struct StepArgs {
+    void* out;
+    const void* q;
+    const void* k_new;
+    const void* v_new;
+    void* k_cache;
+    void* v_cache;
+    int64_t num_blocks;
+    const int32_t* block_table;
+    int32_t max_blocks;
+    const int32_t* cu_seqlens_q;
+    const int32_t* context_lens;
+    int32_t num_seqs, total_q, max_q_len, max_context_len;
+    int32_t num_q_heads, num_kv_heads, head_dim, block_size;
+    float scale;
+    char* ws;  // workspace base
+    WsLayout lay;
+    hipStream_t stream;
+};
+
+// Append new K/V rows into the pools (hdr may be null: no flag reporting).
+hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         int64_t num_blocks, const int32_t* table, int32_t max_blocks,
+                         const int32_t* cu, const int32_t* ctx, int32_t num_seqs,
+                         int32_t total_q, int32_t hkv, int32_t head_dim, int32_t block_size,
+                         int32_t* hdr, hipStream_t stream);
+
+hipError_t launch_gather(const void* k_cache, const void* v_cache, int64_t num_blocks,
+                         const int32_t* table, int32_t max_blocks, const int32_t* seq_lens,
+                         const int64_t* cu_seq_lens, int64_t total_tokens, void* k_out,
+                         void* v_out, int32_t num_seqs, int32_t hkv, int32_t head_dim,
+                         int32_t block_size, hipStream_t stream);
+
+// Work lists for the decode and prefill kernels (zeroes the header flags).
+hipError_t launch_plan(const StepArgs& a);
+// Split-K decode partials (+ direct output for one-partition sequences).
+hipError_t launch_decode(const StepArgs& a);
+// Log-sum-exp merge of the partials of multi-partition decode sequences.
+hipError_t launch_merge(const StepArgs& a);
+// MFMA prefill over chunks of >= 2 rows.
+hipError_t launch_prefill(const StepArgs& a);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace kvc

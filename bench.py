@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of one ragged paged-attention step on one MI355X.
+
+Default workload: the mixed continuous-batching step (token budget 2560):
+4 prefill chunks of 512 rows at cached lengths {0, 512, 1024, 3584} plus 512
+decode rows with context U{128..4096}; 32 q heads / 8 kv heads, head_dim 128,
+bf16, block size 16, physical blocks shuffled.  One step = one call of
+kvc_paged_attention_varlen: append of the 2560 new K/V rows, the MFMA prefill
+kernel, the split-K decode kernel and its merge (plus the planning kernel).
+Inputs are seeded synthetic data already resident in HBM.
+
+Prints one JSON line: whole-step tokens/s, the roofline of the dominant kernel
+(timed with HIP events on the library's stream during the timed steps), the
+decode KV-read bandwidth, the prefill MFMA utilisation, and the CPU oracle
+timed on a bounded sample of the same step on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "mixed-step tokens/s; decode KV-read GB/s vs HBM peak; prefill MFMA util"
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+
+WORKLOADS = {
+    "mixed": ("mixed continuous-batching step: 4 prefill chunks x 512 rows at cached "
+              "lengths {0,512,1024,3584} + 512 decode rows with context U{128..4096}; "
+              "32 q / 8 kv heads, head_dim 128, bf16, block 16", W.mixed),
+    "decode_mha": ("decode batch, Llama-2-7B layer: 64 sequences, 32/32 heads, head_dim 128, "
+                   "context U{512..4096}, block 16", W.decode_mha),
+    "decode_gqa": ("GQA decode: 256 sequences, 32/8 heads, head_dim 128, context lognormal "
+                   "(median 1024, sigma 0.8, clip [16, 8192]), block 16", W.decode_gqa),
+    "long_prefill": ("32768-token prompt as 16 sequential 2048-token chunks; 32/8 heads, "
+                     "head_dim 128, block 16", W.long_prefill),
+    "shared_prefix": ("16 x 256-token suffix chunks over one shared 2048-token prefix; "
+                      "32/8 heads, head_dim 128, block 16", W.shared_prefix),
+}
+
+
+def dev_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def algorithmic(wl, steps):
+    """Algorithmic work of the timed calls (per step = all calls below)."""
+    hkv, hq, a = wl.num_kv_heads, wl.num_q_heads, wl.head_dim
+    dec_bytes = 0
+    pairs = 0
+    tokens = 0
+    for st in steps:
+        ql = st.q_lens.astype(np.int64)
+        c = st.context_lens.astype(np.int64)
+        tokens += int(ql.sum())
+        d = ql == 1
+        dec_bytes += int((c[d] + 1).sum()) * hkv * a * 2 * 2  # K and V, bf16
+        p = ql >= 2
+        # row i of a chunk sees c + i + 1 keys
+        pairs += int((ql[p] * c[p] + ql[p] * (ql[p] + 1) // 2).sum())
+    return {"tokens": tokens, "decode_kv_bytes": dec_bytes, "prefill_pairs": pairs,
+            "prefill_flops": 4 * a * hq * pairs,
+            "append_bytes": tokens * hkv * a * 2 * 2 * 2}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, steps, every):
+    """The oracle as it stands on a row sample of the same step(s)."""
+    import oracle
+    orc = oracle.get()
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()   # harness copy, not timed
+    t_total, rows_total, used = 0.0, 0, 1
+    for st in steps:
+        sel = np.zeros(st.total_q, dtype=bool)
+        sel[::every] = True
+        t0 = time.perf_counter()
+        orc.append(kp, vp, st.k_new, st.v_new, st.block_table, st.cu_seqlens_q, st.context_lens)
+        _, used = orc.attention(st.q, kp, vp, st.block_table, st.cu_seqlens_q, st.context_lens,
+                                wl.scale, row_select=sel,
+                                nthreads=len(os.sched_getaffinity(0)))
+        t_total += time.perf_counter() - t0
+        rows_total += int(sel.sum())
+    return rows_total / t_total, used, rows_total, t_total
+
+
+def host_alloc_cost(wl, steps, reps=20):
+    """Host block allocation for the step (just-in-time table growth of every
+    sequence by its new tokens), timed on the product allocator; the blocks are
+    released after each repetition so every repetition sees the same state."""
+    import batching_kv_append_amd as kvc
+    bs = wl.block_size
+    st = steps[0]
+    need = int(((st.context_lens.astype(np.int64) + st.q_lens + bs - 1) // bs).sum())
+    alloc = kvc.Allocator(need + 64, bs)
+    mb = st.block_table.shape[1]
+    rows = np.full((st.num_seqs, mb), -1, dtype=np.int32)
+    held = np.zeros(st.num_seqs, dtype=np.int32)
+    for s in range(st.num_seqs):
+        held[s] = kvc.kvc_extend_table(alloc, rows[s], 0, int(st.context_lens[s]))
+    ts = []
+    for _ in range(reps):
+        h2 = held.copy()
+        t0 = time.perf_counter()
+        for s in range(st.num_seqs):
+            h2[s] = kvc.kvc_extend_table(alloc, rows[s], int(h2[s]),
+                                         int(st.context_lens[s] + st.q_lens[s]))
+        ts.append(time.perf_counter() - t0)
+        new = np.concatenate([rows[s, held[s]:h2[s]] for s in range(st.num_seqs)])
+        kvc.kvc_free_blocks(alloc, new)
+    alloc.close()
+    return float(np.median(ts) * 1e6)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-every", type=int, default=2,
+                    help="oracle timing uses every n-th row of the step")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this library runs one GPU's share of the step; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported — run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+
+    import batching_kv_append_amd as kvc
+
+    desc, make = WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    wl = make() if args.seed is None else make(seed=args.seed)
+    steps = wl.steps if args.workload != "shared_prefix" else wl.steps[1:]
+    gen_s = time.perf_counter() - t0
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    # ---- device state --------------------------------------------------------
+    k_cache, v_cache = dev_bits(wl.k_pool), dev_bits(wl.v_pool)
+    if args.workload == "shared_prefix":
+        # the prefix is written once (untimed); the timed step is the suffix call
+        st0 = wl.steps[0]
+        ws0 = kvc.new_workspace(st0.num_seqs, st0.total_q, st0.max_q_len, st0.max_context_len,
+                                wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size)
+        q0 = dev_bits(st0.q)
+        kvc.kvc_paged_attention_varlen(torch.empty_like(q0), q0, dev_bits(st0.k_new),
+                                       dev_bits(st0.v_new), k_cache, v_cache,
+                                       dev_i32(st0.block_table), dev_i32(st0.cu_seqlens_q),
+                                       dev_i32(st0.context_lens), wl.scale,
+                                       max_q_len=st0.max_q_len,
+                                       max_context_len=st0.max_context_len, workspace=ws0)
+    calls = []
+    for st in steps:
+        q = dev_bits(st.q)
+        ws = kvc.new_workspace(st.num_seqs, st.total_q, st.max_q_len, st.max_context_len,
+                               wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size)
+        calls.append(dict(out=torch.empty_like(q), q=q, k_new=dev_bits(st.k_new),
+                          v_new=dev_bits(st.v_new), table=dev_i32(st.block_table),
+                          cu=dev_i32(st.cu_seqlens_q), ctx=dev_i32(st.context_lens),
+                          ws=ws, max_q=st.max_q_len, max_c=st.max_context_len))
+    torch.cuda.synchronize()
+
+    def one_step():
+        for c in calls:
+            kvc.kvc_paged_attention_varlen(c["out"], c["q"], c["k_new"], c["v_new"], k_cache,
+                                           v_cache, c["table"], c["cu"], c["ctx"], wl.scale,
+                                           max_q_len=c["max_q"], max_context_len=c["max_c"],
+                                           workspace=c["ws"], stream=stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    for c in calls:
+        assert kvc.kvc_workspace_flags(c["ws"]) == 0
+
+    # ---- timed region -----------------------------------------------------------
+    kvc.kvc_profile_begin(args.steps * len(calls))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phase_ms, ncalls = kvc.kvc_profile_end()
+    assert ncalls == args.steps * len(calls), (ncalls, args.steps * len(calls))
+    per_step_us = {k: v * 1e3 / args.steps for k, v in phase_ms.items()}
+
+    alg = algorithmic(wl, steps)
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = alg["tokens"] * args.steps / elapsed
+
+    dec_us = per_step_us["decode"]
+    merge_us = per_step_us["merge"]
+    pre_us = per_step_us["prefill"]
+    decode = None
+    if alg["decode_kv_bytes"]:
+        gbps = alg["decode_kv_bytes"] / (dec_us * 1e-6) / 1e9
+        decode = {"kv_bytes_per_step": alg["decode_kv_bytes"], "partial_us": dec_us,
+                  "merge_us": merge_us, "kernel_gbps": gbps,
+                  "with_merge_gbps": alg["decode_kv_bytes"] / ((dec_us + merge_us) * 1e-6) / 1e9,
+                  "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
+    prefill = None
+    if alg["prefill_flops"]:
+        tf = alg["prefill_flops"] / (pre_us * 1e-6) / 1e12
+        prefill = {"flops_per_step": alg["prefill_flops"], "visible_pairs_per_head":
+                   alg["prefill_pairs"], "kernel_us": pre_us, "tflops": tf,
+                   "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+
+    launches = len(calls)  # per step; each call launches each kernel at most once
+    if decode and (not prefill or dec_us >= pre_us):
+        roofline = {"bound": "hbm", "kernel": "decode_kernel (split-K partials)",
+                    "achieved": decode["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": decode["frac_hbm_peak"], "traffic": None,
+                    "algorithmic_bytes_per_launch": alg["decode_kv_bytes"] / launches,
+                    "avg_launch_us": dec_us / launches}
+    else:
+        roofline = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA)",
+                    "achieved": prefill["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": prefill["frac_mfma_peak"], "traffic": None,
+                    "algorithmic_flops_per_launch": alg["prefill_flops"] / launches,
+                    "avg_launch_us": pre_us / launches}
+
+    st0 = steps[0]
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the pages' workloads)",
+        "config": {"workload": desc, "name": args.workload, "calls_per_step": len(calls),
+                   "num_seqs": int(st0.num_seqs), "tokens_per_step": alg["tokens"],
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "pool_blocks": wl.num_blocks},
+        "roofline": roofline,
+        "decode": decode, "prefill": prefill,
+        "kernels_us_per_step": per_step_us,
+        "host_alloc_us_per_step": host_alloc_cost(wl, steps),
+        "input_gen_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        every = max(1, args.cpu_sample_every)
+        if args.workload == "long_prefill":
+            every = max(every, 64)
+        rate, used, nrows, secs = cpu_baseline(wl, steps, every)
+        result["cpu_baseline"] = {
+            "value": rate, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"every {every}-th row of the step ({nrows} rows, {secs:.1f} s, fp64 "
+                      f"append + attention, OpenMP); host CPU {cpu_model()}"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,85 @@
+"""Host block allocator: free list, reference counts, all-or-nothing
+allocation, just-in-time table growth (CPU only)."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def kvc():
+    import batching_kv_append_amd as m
+    return m
+
+
+def test_alloc_share_free_cycle(kvc):
+    a = kvc.Allocator(16, 16)
+    ids = kvc.kvc_alloc_blocks(a, 10)
+    assert len(set(ids.tolist())) == 10 and kvc.kvc_num_free_blocks(a) == 6
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_alloc_blocks(a, 7)
+    assert e.value.status == kvc.KVC_ERR_OOM and kvc.kvc_num_free_blocks(a) == 6
+    kvc.kvc_share_blocks(a, ids[:4])
+    assert [kvc.kvc_block_refcount(a, i) for i in ids[:5]] == [2, 2, 2, 2, 1]
+    kvc.kvc_free_blocks(a, ids)
+    assert kvc.kvc_num_free_blocks(a) == 12
+    kvc.kvc_free_blocks(a, ids[:4])
+    assert kvc.kvc_num_free_blocks(a) == 16
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_free_blocks(a, ids[:1])
+    assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_just_in_time_growth(kvc):
+    """A sequence takes a new block exactly when its last block is full."""
+    a = kvc.Allocator(64, 16)
+    row = np.full(8, -1, dtype=np.int32)
+    held = 0
+    taken = []
+    for L in range(1, 129):
+        before = kvc.kvc_num_free_blocks(a)
+        held = kvc.kvc_extend_table(a, row, held, L)
+        taken.append(before - kvc.kvc_num_free_blocks(a))
+        assert held == (L + 15) // 16
+    assert [i + 1 for i, t in enumerate(taken) if t] == [1, 17, 33, 49, 65, 81, 97, 113]
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_extend_table(a, row, held, 129)
+
+
+def test_prefix_sharing_footprint(kvc):
+    """16 sequences share a 2048-token prefix (128 blocks) written once, each
+    with a 256-token suffix: 128 + 16*16 = 384 blocks instead of 16*144."""
+    a = kvc.Allocator(4096, 16)
+    prefix = np.full(128, -1, dtype=np.int32)
+    kvc.kvc_extend_table(a, prefix, 0, 2048)
+    tables = []
+    for s in range(16):
+        row = np.full(144, -1, dtype=np.int32)
+        row[:128] = prefix
+        if s > 0:
+            kvc.kvc_share_blocks(a, prefix)
+        kvc.kvc_extend_table(a, row, 128, 2048 + 256)
+        tables.append(row)
+    assert 4096 - kvc.kvc_num_free_blocks(a) == 384
+    assert all(kvc.kvc_block_refcount(a, int(b)) == 16 for b in prefix)
+    assert kvc.kvc_block_refcount(a, int(tables[3][130])) == 1
+    for row in tables:
+        kvc.kvc_free_blocks(a, row)
+    assert kvc.kvc_num_free_blocks(a) == 4096
+
+
+def test_native_driver_under_sanitizers(tmp_path):
+    exe = tmp_path / "allocator_driver"
+    srcs = [os.path.join(ROOT, "tests", "native", "allocator_driver.cpp"),
+            os.path.join(ROOT, "batching_kv_append_amd", "csrc", "allocator.cpp"),
+            os.path.join(ROOT, "batching_kv_append_amd", "csrc", "status.cpp")]
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-I" + os.path.join(ROOT, "include"),
+           "-I" + os.path.join(ROOT, "batching_kv_append_amd", "csrc"), *srcs, "-o", str(exe)]
+    subprocess.run(cmd, check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "allocator driver ok" in r.stdout

@@ -1,0 +1,124 @@
+"""Attention parity: the HIP path against the fp64 oracle, element by element.
+
+Bar: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3 over the
+compared rows, bf16 inputs and bf16 output.  The small cases span several
+tiles, partitions and ragged tails; the five workloads run at full size
+(every row for the decode and mixed steps; sampled rows, computed one by one
+by the oracle, for the 32K-token prompt and the shared-prefix step)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import compare, oracle_run, run_steps
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvc():
+    import batching_kv_append_amd as m
+    return m
+
+
+def _case(kvc, orc, name, specs, hq, hkv, a, bs, seed=7, scale=None):
+    wl = W.make_step_workload(name, specs, num_q_heads=hq, num_kv_heads=hkv, head_dim=a,
+                              block_size=bs, seed=seed, scale=scale)
+    (g,), _, _ = run_steps(kvc, wl)
+    (r,), _, _ = oracle_run(orc, wl)
+    return compare(g, r, what=name)
+
+
+DEC_LENS = [0, 1, 5, 15, 16, 17, 255, 256, 257, 511, 512, 600, 1500]
+PRE_SPECS = [(0, 2), (0, 63), (0, 64), (0, 65), (5, 130), (300, 200), (17, 1)]
+MIXED_SPECS = [(10, 0), (0, 1), (17, 5), (64, 1), (0, 0), (129, 77), (3000, 1), (0, 300),
+               (700, 2), (255, 1), (1024, 129)]
+SMALL = [
+    ("decode_mha", [(c, 1) for c in DEC_LENS], 4, 4, 128, 16),
+    ("decode_gqa2_bs4", [(c, 1) for c in DEC_LENS], 4, 2, 128, 4),
+    ("decode_gqa4", [(c, 1) for c in DEC_LENS], 8, 2, 128, 16),
+    ("decode_gqa8", [(c, 1) for c in DEC_LENS], 16, 2, 128, 16),
+    ("decode_gqa16", [(c, 1) for c in DEC_LENS], 16, 1, 128, 16),
+    ("prefill_mha", PRE_SPECS, 2, 2, 128, 16),
+    ("prefill_gqa2", PRE_SPECS, 4, 2, 128, 16),
+    ("prefill_gqa4_bs4", PRE_SPECS, 8, 2, 128, 4),
+    ("prefill_gqa8", PRE_SPECS, 8, 1, 128, 16),
+    ("mixed_gqa4", MIXED_SPECS, 8, 2, 128, 16),
+    ("mixed_mha_bs4", MIXED_SPECS, 2, 2, 128, 4),
+    ("a16_mixed", [(0, 7), (4, 3), (7, 1), (30, 1), (100, 40), (0, 1), (257, 1)], 1, 1, 16, 4),
+    ("a16_gqa2_bs16", [(0, 7), (4, 3), (7, 1), (30, 1), (100, 40), (600, 1)], 4, 2, 16, 16),
+    ("a16_gqa4_bs4", [(0, 70), (33, 1), (2, 2)], 4, 1, 16, 4),
+]
+
+
+@pytest.mark.parametrize("name,specs,hq,hkv,a,bs", SMALL, ids=[c[0] for c in SMALL])
+def test_small(kvc, orc, name, specs, hq, hkv, a, bs):
+    _case(kvc, orc, name, specs, hq, hkv, a, bs)
+
+
+def test_scale_variants(kvc, orc):
+    _case(kvc, orc, "scale0", [(20, 1), (0, 40), (300, 1)], 4, 2, 128, 16, scale=0.0)
+    _case(kvc, orc, "scale_big", [(20, 1), (0, 40), (300, 1)], 4, 2, 128, 16, scale=0.5)
+
+
+def test_toy_chunked_then_decode(kvc, orc):
+    """Chunks of 4 and 3 tokens (block size 4), then 8 decode calls; every call
+    against the oracle and the chunked rows against the unchunked prefill."""
+    wl = W.toy(0)
+    g, _, _ = run_steps(kvc, wl)
+    r, _, _ = oracle_run(orc, wl)
+    for i, (gi, ri) in enumerate(zip(g, r)):
+        compare(gi, ri, what=f"toy call {i}")
+    qb, kb, vb = wl.extra["full"]
+    un = W.Step(q=qb[:7].copy(), k_new=kb[:7].copy(), v_new=vb[:7].copy(),
+                cu_seqlens_q=np.array([0, 7], np.int32), context_lens=np.array([0], np.int32),
+                block_table=wl.extra["table"])
+    (ru,), _, _ = oracle_run(orc, wl, [un])
+    compare(np.concatenate(g[:2]), ru, what="toy chunked vs unchunked")
+    # decode step t equals the last row of the unchunked prefill over t+1 tokens
+    for t in range(7, 15):
+        un = W.Step(q=qb[:t + 1].copy(), k_new=kb[:t + 1].copy(), v_new=vb[:t + 1].copy(),
+                    cu_seqlens_q=np.array([0, t + 1], np.int32),
+                    context_lens=np.array([0], np.int32), block_table=wl.extra["table"])
+        (ru,), _, _ = oracle_run(orc, wl, [un])
+        compare(g[2 + t - 7], ru[t:t + 1], what=f"toy decode {t}")
+
+
+@pytest.mark.parametrize("cfg", ["decode_mha", "decode_gqa", "mixed"])
+def test_full_workload(kvc, orc, cfg):
+    wl = getattr(W, cfg)()
+    (g,), _, _ = run_steps(kvc, wl)
+    (r,), _, _ = oracle_run(orc, wl)
+    mx, mean = compare(g, r, what=cfg)
+    print(f"{cfg}: max {mx:.3e} mean {mean:.3e}", flush=True)
+
+
+def _sample_rows(n, rng, k=6):
+    rows = {0, 1, n // 2, n - 2, n - 1} | set(rng.integers(0, n, size=k).tolist())
+    sel = np.zeros(n, dtype=bool)
+    sel[[r for r in rows if 0 <= r < n]] = True
+    return sel
+
+
+def test_long_prefill_chunks_sampled(kvc, orc):
+    """32768-token prompt in 16 chunks of 2048 (cached length 2048*k)."""
+    wl = W.long_prefill()
+    g, _, _ = run_steps(kvc, wl)
+    rng = np.random.default_rng(5)
+    sels = [_sample_rows(st.total_q, rng) for st in wl.steps]
+    r, _, _ = oracle_run(orc, wl, row_select=sels)
+    for k, (gk, rk, sel) in enumerate(zip(g, r, sels)):
+        compare(gk, rk, rows=sel, what=f"chunk {k}")
+
+
+def test_shared_prefix_sampled(kvc, orc):
+    """16 sequences over one refcounted 2048-token prefix, 256-token suffixes."""
+    wl = W.shared_prefix()
+    g, _, _ = run_steps(kvc, wl)
+    rng = np.random.default_rng(6)
+    sels = [_sample_rows(st.total_q, rng, k=40) for st in wl.steps]
+    r, _, _ = oracle_run(orc, wl, row_select=sels)
+    for k, (gk, rk, sel) in enumerate(zip(g, r, sels)):
+        compare(gk, rk, rows=sel, what=f"call {k}")

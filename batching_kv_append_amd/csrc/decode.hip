@@ -20,9 +20,9 @@
 //   * q.k partial dots are reduced across the 16 lanes with DPP row
 //     operations; softmax is online per lane group, with one cross-group
 //     merge per work unit.
-// Work units are claimed from a device counter by persistent waves, so the
-// host needs no copy of the lengths and load balance does not depend on the
-// length distribution.
+// The planning kernel lists the work units on the device, so the host needs no
+// copy of the lengths; each wave takes one unit, and the hardware dispatcher
+// hands the next workgroup to whichever compute unit frees up first.
 #include <hip/hip_runtime.h>
 
 #include "kvc_launch.h"
@@ -122,7 +122,6 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
         if (cu[0] != 0 || cu[num_seqs] != total_q) flags |= FLAG_CU_SEQLENS;
         hdr[HDR_N_DEC] = (int)min((int64_t)carry[0], cap_dec);
         hdr[HDR_N_PRE] = (int)min((int64_t)carry[1], cap_pre);
-        hdr[HDR_DEC_NEXT] = 0;
         hdr[HDR_N_MERGE] = carry[2];
         if (flags) atomicOr(hdr + HDR_FLAGS, flags);
     }
@@ -165,12 +164,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     const int r = lane / LPR;
     const int c8 = lane % LPR;
     const int64_t n_units = (int64_t)P.hdr[HDR_N_DEC] * P.hkv * P.HC;
-
-    for (;;) {
-        int u = 0;
-        if (lane == 0) u = atomicAdd(P.hdr + HDR_DEC_NEXT, 1);
-        u = __builtin_amdgcn_readfirstlane(u);  // wave-uniform from here on
-        if (u >= n_units) break;
+    // One wave per work unit; the grid covers the host-side upper bound and
+    // waves past the planned count leave at once.  The unit index comes from
+    // the launch coordinates only, so it is uniform by construction.
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (u >= n_units) return;
+    {
         const int hc = u % P.HC;
         const int kvh = (u / P.HC) % P.hkv;
         const int item = u / (P.HC * P.hkv);
@@ -451,12 +450,12 @@ hipError_t launch_decode(const StepArgs& a) {
     p.G = G;
     p.HC = G / GW;
     p.scale_log2 = a.scale * 1.4426950408889634f;
-    // Persistent grid: enough waves to cover the chip, never more than units.
+    // One wave per unit over the upper bound of units (4 waves per workgroup).
     const int64_t units = a.lay.cap_dec * a.num_kv_heads * p.HC;
-    const int64_t waves_wanted = (int64_t)device_cu_count() * 16;
-    const int64_t waves = units < waves_wanted ? units : waves_wanted;
-    const int grid = (int)((waves + 3) / 4);
-    if (grid <= 0) return hipSuccess;
+    const int64_t grid64 = (units + 3) / 4;
+    if (grid64 <= 0) return hipSuccess;
+    if (grid64 > INT32_MAX) return hipErrorInvalidValue;
+    const int grid = (int)grid64;
     if (a.head_dim == 128) {
         if (a.block_size == 16) launch_decode_gw<128, 16>(a, p, GW, grid);
         else launch_decode_gw<128, 4>(a, p, GW, grid);

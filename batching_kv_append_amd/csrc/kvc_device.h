@@ -12,7 +12,7 @@ namespace kvc {
 enum HeaderSlot : int {
     HDR_N_DEC = 0,       // decode work items (sequence, partition)
     HDR_N_PRE = 1,       // prefill work items (sequence, position tile)
-    HDR_DEC_NEXT = 2,    // next decode unit to claim (persistent kernel)
+    HDR_UNUSED = 2,
     HDR_N_MERGE = 3,     // decode sequences split into >1 partition
     HDR_FLAGS = 4,       // error flags (kvc_workspace_flags)
     HDR_WORDS = 64

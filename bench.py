@@ -145,7 +145,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-every", type=int, default=2,
                     help="oracle timing uses every n-th row of the step")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device-to-device copies (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this library runs one GPU's share of the step; --gpus {args.gpus} "

@@ -135,6 +135,31 @@ def host_alloc_cost(wl, steps, reps=20):
     return float(np.median(ts) * 1e6)
 
 
+KERNEL_SOURCES = {
+    "decode_kernel": ["batching_kv_append_amd/csrc/decode.hip", "batching_kv_append_amd/csrc/kvc_device.h"],
+    "prefill_kernel": ["batching_kv_append_amd/csrc/prefill.hip", "batching_kv_append_amd/csrc/kvc_device.h"],
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summaries in profiles/,
+    or None when none was taken on the kernel's current source."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    key = f"traffic {kernel} src_sha256_16={h.hexdigest()[:16]} "
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith(key):
+                    fields = dict(kv.split("=", 1) for kv in line.split()[2:])
+                    return int(fields["bytes_per_launch"])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,13 +276,14 @@ def main():
     if decode and (not prefill or dec_us >= pre_us):
         roofline = {"bound": "hbm", "kernel": "decode_kernel (split-K partials)",
                     "achieved": decode["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": decode["frac_hbm_peak"], "traffic": None,
+                    "frac": decode["frac_hbm_peak"], "traffic": measured_traffic("decode_kernel"),
                     "algorithmic_bytes_per_launch": alg["decode_kv_bytes"] / launches,
                     "avg_launch_us": dec_us / launches}
     else:
         roofline = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA)",
                     "achieved": prefill["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": prefill["frac_mfma_peak"], "traffic": None,
+                    "unit": "TFLOP/s", "frac": prefill["frac_mfma_peak"],
+                    "traffic": measured_traffic("prefill_kernel"),
                     "algorithmic_flops_per_launch": alg["prefill_flops"] / launches,
                     "avg_launch_us": pre_us / launches}
 

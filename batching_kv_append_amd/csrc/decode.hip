@@ -36,12 +36,15 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int PLAN_THREADS = 1024;
 
+constexpr int COST_BUCKETS = 1024;  // prefill cost histogram (key tiles, clamped)
+
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ ctx, int32_t num_seqs,
     int32_t total_q, int32_t max_q_len, int32_t max_context_len, int32_t span, int64_t cap_dec,
     int64_t cap_pre, int32_t* hdr, int32_t* dec_base, int2* dec_items, int2* pre_items,
-    int32_t* merge_list) {
+    int2* pre_sorted, int32_t* merge_list) {
     __shared__ int sc[3][PLAN_THREADS];
+    __shared__ int hist[COST_BUCKETS];
     __shared__ int carry[3];
     __shared__ int flags;
     const int tid = threadIdx.x;
@@ -118,10 +121,42 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
         }
         __syncthreads();
     }
+    // Order the prefill work costliest first (counting sort on the number of
+    // 64-key tiles a workgroup walks), so the longest workgroups start first
+    // and the short ones fill the tail.
+    const int npre = (int)min((int64_t)carry[1], cap_pre);
+    for (int b = tid; b < COST_BUCKETS; b += PLAN_THREADS) hist[b] = 0;
+    __syncthreads();
+    auto bucket_of = [&](int2 item) {
+        const int q = cu[item.x + 1] - cu[item.x];
+        const int64_t keys = (int64_t)ctx[item.x] + min((item.y + 1) * span, q);
+        const int64_t tiles = (keys + PREFILL_TK - 1) / PREFILL_TK;
+        return COST_BUCKETS - 1 - (int)min(tiles, (int64_t)COST_BUCKETS - 1);
+    };
+    for (int i = tid; i < npre; i += PLAN_THREADS) atomicAdd(&hist[bucket_of(pre_items[i])], 1);
+    __syncthreads();
+    {  // exclusive scan of the histogram (one bucket per thread)
+        const int v = tid < COST_BUCKETS ? hist[tid] : 0;
+        sc[0][tid] = v;
+        __syncthreads();
+        for (int off = 1; off < PLAN_THREADS; off <<= 1) {
+            const int a0 = tid >= off ? sc[0][tid - off] : 0;
+            __syncthreads();
+            sc[0][tid] += a0;
+            __syncthreads();
+        }
+        if (tid < COST_BUCKETS) hist[tid] = sc[0][tid] - v;
+    }
+    __syncthreads();
+    for (int i = tid; i < npre; i += PLAN_THREADS) {
+        const int2 item = pre_items[i];
+        const int at = atomicAdd(&hist[bucket_of(item)], 1);
+        pre_sorted[at] = item;
+    }
     if (tid == 0) {
         if (cu[0] != 0 || cu[num_seqs] != total_q) flags |= FLAG_CU_SEQLENS;
         hdr[HDR_N_DEC] = (int)min((int64_t)carry[0], cap_dec);
-        hdr[HDR_N_PRE] = (int)min((int64_t)carry[1], cap_pre);
+        hdr[HDR_N_PRE] = npre;
         hdr[HDR_N_MERGE] = carry[2];
         if (flags) atomicOr(hdr + HDR_FLAGS, flags);
     }
@@ -337,6 +372,266 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode partial kernel on the matrix cores (head_dim 128).
+//
+// Both products of a decode step are small matrix products once the query
+// heads that share a kv head are stacked as columns (up to 16):
+//   S^T[token][head] = K[token][:] . Q^T[:][head]      v_mfma_f32_16x16x32_bf16
+//   O^T[dim][head]  += V^T[dim][token] . P^T[token][head]
+// K goes straight from global memory into the A operand (lane l owns token
+// l%16 of a 16-token block and 8 dims of each 32-dim step); the score
+// registers of a lane (head l%16, tokens 4g..4g+3 of each block, g = l/16)
+// are already the B operand of the second product for a 32-token step, with
+// the key order {4g..4g+3, 16+4g..16+4g+3}; V is transposed through a
+// per-wave 8 KiB LDS tile in that same order.  The four lanes of a head
+// column share one running maximum (two lane exchanges per step), so the
+// weights summed by one matrix instruction share one scale.  The VALU work per
+// 32-token step is about 80 instructions, far under the bytes' HBM time.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);  // a.lo | b.lo << 16
+}
+__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.hi | b.hi << 16
+}
+
+template <int BS>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
+    constexpr int A = 128;
+    constexpr int CPR = A / 8;              // 16-byte chunks per row
+    constexpr int STEP = 32;                // tokens per matrix step
+    constexpr int NT = DECODE_PART / BS;    // table entries per partition
+    constexpr float RESCALE_SLACK = 8.0f;   // log2 units: weights stay < 2^8
+    static_assert(NT <= 64, "table slice must fit one VGPR");
+    static_assert(BS % 4 == 0, "4 consecutive tokens must share a block");
+
+    // per wave: V^T of one 32-token step, [dim][4 chunks of 8 tokens], 64 B rows
+    __shared__ uint4 sVt[4][A * 4];
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15;  // head column
+    const int g = lane >> 4;    // token group: tokens 4g..4g+3 of each 16-token block
+    const int64_t n_units = (int64_t)P.hdr[HDR_N_DEC] * P.hkv * P.HC;
+    const int64_t u = (int64_t)blockIdx.x * 4 + wave;
+    if (u >= n_units) return;
+    uint4* vt = &sVt[wave][0];
+
+    const int GW = P.G / P.HC;  // heads of this wave (<= 16)
+    const int hc = u % P.HC;
+    const int kvh = (u / P.HC) % P.hkv;
+    const int item = u / (P.HC * P.hkv);
+    const int2 it = P.items[item];
+    const int s = it.x, part = it.y;
+    const int L = P.ctx[s] + 1;
+    const int row = P.cu[s];
+    const int nparts = (L + DECODE_PART - 1) / DECODE_PART;
+    const int t0 = part * DECODE_PART;
+    const int t1 = min(L, t0 + DECODE_PART);
+    const int h0 = kvh * P.G + hc * GW;
+    const float cs = P.scale_log2;
+    const bool pos_scale = cs > 0.f;
+
+    // table slice: lane i holds entry (t0 / BS + i)
+    const int lb0 = t0 / BS;
+    const int nlb = (t1 - t0 + BS - 1) / BS;
+    int tbl = -1;
+    if (lane < nlb && lane < NT) {
+        const int64_t lb = lb0 + lane;
+        if (lb < P.max_blocks) tbl = P.table[(int64_t)s * P.max_blocks + lb];
+    }
+
+    // Q^T operand: column col = head h0+col (zero past GW), dims 32ks + 8g .. +7
+    uint4 qb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        qb[ks] = make_uint4(0, 0, 0, 0);
+        if (col < GW)
+            qb[ks] = *reinterpret_cast<const uint4*>(
+                P.q + (((int64_t)row * P.hq + h0 + col) * A + ks * 32 + g * 8));
+    }
+
+    f32x4_t o[8];  // O^T rows 16dt + 4g + r, column col
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -1.0e30f, lsum = 0.f;
+    int bad = 0;
+
+    // Block id of token t (< t1) through the table slice.  With 16-token
+    // blocks every lane of a 16-token group asks for the same block, so the
+    // caller passes the group's first (clamped) token and a uniform readlane
+    // serves it; smaller blocks take a per-lane shuffle.
+    auto block_of = [&](int t, int t_group) -> int64_t {
+        if constexpr (BS == 16) {
+            return __builtin_amdgcn_readlane(tbl, t_group / BS - lb0);
+        } else {
+            (void)t_group;
+            return __shfl(tbl, (t / BS - lb0) & 63, 64);
+        }
+    };
+
+    for (int tc = t0; tc < t1; tc += STEP) {
+        // ---- K: two 16-token blocks x four 32-dim steps -------------------
+        uint4 kb[2][4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int t = min(tc + 16 * b + col, t1 - 1);
+            int64_t blk = block_of(t, min(tc + 16 * b, t1 - 1));
+            if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
+            const uint4* kp = P.k_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + g;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kb[b][ks] = kp[ks * 4];
+        }
+        // ---- V: token groups g and g+4 (4 tokens each) x chunk col --------
+        uint4 vb[2][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int tg = g + 4 * hh;
+            const int t = min(tc + 4 * tg, t1 - 1);
+            int64_t blk = block_of(t, min(tc + 16 * hh, t1 - 1));
+            if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
+            const uint4* vp = P.v_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col;
+            if (tc + 4 * tg + 3 < t1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vb[hh][j] = vp[j * CPR];
+            } else {  // rows past the end repeat the last row (their weight is 0)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    vb[hh][j] = vp[(min(tc + 4 * tg + j, t1 - 1) - t) * CPR];
+            }
+        }
+
+        // ---- S^T for the two blocks ------------------------------------------
+        f32x4_t sc[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            sc[b] = mfma16(kb[b][0], qb[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int ks = 1; ks < 4; ++ks) sc[b] = mfma16(kb[b][ks], qb[ks], sc[b]);
+        }
+
+        // ---- V^T into LDS (this wave's tile): 8-byte units of 4 tokens ------
+        // The 4x8 transpose is written as vector interleaves of whole rows
+        // (element-wise extracts would let the optimizer split each 16-byte
+        // row load into four 4-byte loads).
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const u16x8_t r0 = __builtin_bit_cast(u16x8_t, vb[hh][0]);
+            const u16x8_t r1 = __builtin_bit_cast(u16x8_t, vb[hh][1]);
+            const u16x8_t r2 = __builtin_bit_cast(u16x8_t, vb[hh][2]);
+            const u16x8_t r3 = __builtin_bit_cast(u16x8_t, vb[hh][3]);
+            // word e of t01 = (row0[e], row1[e]); of t23 = (row2[e], row3[e])
+            const u32x8_t t01 = __builtin_bit_cast(u32x8_t, __builtin_shufflevector(
+                r0, r1, 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15));
+            const u32x8_t t23 = __builtin_bit_cast(u32x8_t, __builtin_shufflevector(
+                r2, r3, 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15));
+            uint2* vt2 = reinterpret_cast<uint2*>(vt);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = col * 8 + e;
+                // row d, 16-byte chunk g (tokens 4g.. and 16+4g..), half hh
+                vt2[(d * 4 + (g ^ ((d >> 2) & 3))) * 2 + hh] = make_uint2(t01[e], t23[e]);
+            }
+        }
+
+        // ---- online softmax of this lane's column ----------------------------
+        const bool tail = tc + STEP > t1;
+        float v8[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            v8[r] = sc[0][r];
+            v8[4 + r] = sc[1][r];
+        }
+        if (!pos_scale) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) v8[r] *= cs;
+        }
+        if (tail) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int t = tc + (r >> 2) * 16 + 4 * g + (r & 3);
+                if (t >= t1) v8[r] = -INFINITY;
+            }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(v8[0], v8[1]), fmaxf(v8[2], v8[3])),
+                         fmaxf(fmaxf(v8[4], v8[5]), fmaxf(v8[6], v8[7])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float cand = pos_scale ? mx * cs : mx;
+        const bool grow = cand > m + RESCALE_SLACK;
+        if (__any(grow)) {
+            const float m_new = grow ? cand : m;
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            m = m_new;
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        }
+        const float mc = pos_scale ? cs : 1.f;
+        float p[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(fmaf(v8[r], mc, -m));
+            lsum += p[r];
+        }
+        uint4 pb;
+        pb.x = pack_bf16x2(p[0], p[1]);
+        pb.y = pack_bf16x2(p[2], p[3]);
+        pb.z = pack_bf16x2(p[4], p[5]);
+        pb.w = pack_bf16x2(p[6], p[7]);
+
+        // ---- O^T += V^T P^T ------------------------------------------------------
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const int d = dt * 16 + col;
+            const uint4 a = vt[d * 4 + (g ^ ((d >> 2) & 3))];
+            o[dt] = mfma16(a, pb, o[dt]);
+        }
+    }
+    if (bad && lane == 0) set_flag(P.hdr, FLAG_BAD_BLOCK);
+
+    // ---- column totals and output ----------------------------------------------
+    float lt = lsum + __shfl_xor(lsum, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (col < GW) {
+        const int h = h0 + col;
+        if (nparts == 1) {
+            const float inv = 1.f / lt;
+            uint16_t* orow = P.out + ((int64_t)row * P.hq + h) * A;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                uint2 v;
+                v.x = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+                v.y = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+                *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * g) = v;
+            }
+        } else {
+            const int64_t slot = (int64_t)item * P.hq + h;
+            float* acc = P.ws_acc + slot * A;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                *reinterpret_cast<float4*>(acc + dt * 16 + 4 * g) =
+                    make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+            if (g == 0) {
+                P.ws_ml[slot * 2] = m;
+                P.ws_ml[slot * 2 + 1] = lt;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Merge kernel: one wave per (multi-partition decode sequence, query head).
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // ---------------------------------------------------------------------------
@@ -411,7 +706,12 @@ void launch_decode_gw(const StepArgs& a, const DecodeParams& p, int GW, int grid
 
 }  // namespace
 
-int decode_heads_per_wave(int G) {
+int decode_heads_per_wave(int G, int head_dim) {
+    if (head_dim == 128) {  // matrix path: the largest divisor of G that is <= 16
+        for (int gw = G < 16 ? G : 16; gw > 1; --gw)
+            if (G % gw == 0) return gw;
+        return 1;
+    }
     return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
@@ -423,14 +723,14 @@ hipError_t launch_plan(const StepArgs& a) {
                        prefill_span(G), a.lay.cap_dec, a.lay.cap_pre,
                        (int32_t*)(ws + a.lay.hdr), (int32_t*)(ws + a.lay.dec_base),
                        (int2*)(ws + a.lay.dec_items), (int2*)(ws + a.lay.pre_items),
-                       (int32_t*)(ws + a.lay.merge_list));
+                       (int2*)(ws + a.lay.pre_sorted), (int32_t*)(ws + a.lay.merge_list));
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const StepArgs& a) {
     char* ws = a.ws;
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int GW = decode_heads_per_wave(G);
+    const int GW = decode_heads_per_wave(G, a.head_dim);
     DecodeParams p;
     p.q = (const uint16_t*)a.q;
     p.out = (uint16_t*)a.out;
@@ -457,8 +757,10 @@ hipError_t launch_decode(const StepArgs& a) {
     if (grid64 > INT32_MAX) return hipErrorInvalidValue;
     const int grid = (int)grid64;
     if (a.head_dim == 128) {
-        if (a.block_size == 16) launch_decode_gw<128, 16>(a, p, GW, grid);
-        else launch_decode_gw<128, 4>(a, p, GW, grid);
+        if (a.block_size == 16)
+            hipLaunchKernelGGL(decode_mfma_kernel<16>, dim3(grid), dim3(256), 0, a.stream, p);
+        else
+            hipLaunchKernelGGL(decode_mfma_kernel<4>, dim3(grid), dim3(256), 0, a.stream, p);
     } else {
         if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);
         else launch_decode_gw<16, 4>(a, p, GW, grid);

@@ -31,11 +31,11 @@ constexpr int DECODE_PART = 256;
 
 // Prefill: each wave owns one query head and QW consecutive positions; a
 // workgroup of 4 waves covers HPW heads x (4/HPW) position blocks.
-constexpr int PREFILL_QW = 64;
+constexpr int PREFILL_QW = 32;
 constexpr int PREFILL_TK = 64;  // keys per LDS tile
 
 struct WsLayout {
-    size_t hdr, dec_base, dec_items, pre_items, merge_list, ml, acc, total;
+    size_t hdr, dec_base, dec_items, pre_items, pre_sorted, merge_list, ml, acc, total;
     int64_t cap_dec, cap_pre;
 };
 
@@ -57,6 +57,7 @@ inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context
     w.dec_base = off;   off = align_up(off + (size_t)num_seqs * 4, 256);
     w.dec_items = off;  off = align_up(off + (size_t)w.cap_dec * 8, 256);
     w.pre_items = off;  off = align_up(off + (size_t)w.cap_pre * 8, 256);
+    w.pre_sorted = off; off = align_up(off + (size_t)w.cap_pre * 8, 256);
     w.merge_list = off; off = align_up(off + (size_t)num_seqs * 4, 256);
     w.ml = off;         off = align_up(off + (size_t)w.cap_dec * num_q_heads * 2 * 4, 256);
     w.acc = off;        off = align_up(off + (size_t)w.cap_dec * num_q_heads * head_dim * 4, 256);

@@ -14,18 +14,24 @@
 // Computing the transposed scores makes each lane own one query column: its
 // 16 accumulator registers per 32-key block are exactly the 8+8 k-slots of the
 // B operand of the next product (the key order inside a 16-key step only has
-// to agree between P^T and V^T, which reads its keys with the same order), so
-// P never leaves the registers.  Softmax statistics are per lane (one column)
-// with one exchange with lane^32 per 64-key tile.
+// to agree between P^T and V^T, which reads its keys in the same order), so P
+// never leaves the registers.  Softmax statistics are per lane (one column)
+// with one exchange with lane^32 per 64-key tile.  The running maximum is
+// only moved when it grows by more than 2^8 (weights stay below 256); the
+// numerator and the denominator share it, so the result is unchanged and the
+// accumulator rescale is rare.
 //
 // Work: one workgroup = 4 waves = HPW query heads of one kv group x (4/HPW)
-// blocks of PREFILL_QW = 64 positions; each wave owns one (head, 64
-// positions) and two 32-column MFMA tiles.  K/V tiles of 64 keys (four 16-token
-// blocks, gathered through the block table) are staged in LDS once per
-// workgroup and shared by the HPW heads of the group (GQA, e2hang/Notes
-// "MQA与GQA").  K is stored row-major with a 16-byte XOR swizzle; V is stored
-// transposed ([dim][key]) with an 8-byte XOR swizzle, so both operand reads
-// are bank-conflict free.
+// blocks of QW = 32 positions; each wave owns one (head, 32 positions).  K/V
+// tiles of 64 keys (gathered block by block through the block table) are
+// staged in LDS, double-buffered, once per workgroup and shared by the HPW
+// heads of the group (GQA, e2hang/Notes "MQA与GQA").  K is stored row-major
+// with a 16-byte XOR swizzle; V is stored transposed ([dim][key], keys
+// permuted so a lane's eight P.V keys are one 16-byte chunk) with a 16-byte
+// XOR swizzle, so both operand reads are single conflict-free ds_read_b128.
+// Each loading thread owns 4 consecutive keys x 8 dims: its V^T stores are
+// eight 8-byte writes.  The planning kernel lists the
+// workgroups costliest first.
 #include <hip/hip_runtime.h>
 
 #include "kvc_launch.h"
@@ -45,11 +51,11 @@ struct PrefillParams {
     const int32_t* table;
     const int32_t* cu;
     const int32_t* ctx;
-    const int32_t* hdr;
+    int32_t* hdr;
     const int2* items;
     int64_t num_blocks;
     int32_t max_blocks, hq, hkv, G, HC;
-    float scale_log2;
+    float scale_log2;  // scale * log2(e)
 };
 
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
@@ -57,25 +63,42 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Low / high 16-bit halves of two words, packed: (a.lo | b.lo << 16), (a.hi | b.hi << 16).
+// One v_perm_b32 each: bytes 0-3 of the selector space are `a`, 4-7 are `b`.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// XOR swizzle of the 16-byte chunks of V^T row d.  Reads: 8 (or 16)
+// consecutive rows d at one logical chunk hit distinct bank groups.  Writes:
+// rows d = 8*cc + e of one e over cc = 0..7 hit distinct chunks.
+__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+
 template <int A, int BS, int HPW>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams P) {
-    constexpr int TK = PREFILL_TK;         // keys per tile
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
+    constexpr int TK = PREFILL_TK;         // keys per tile (64)
     constexpr int CPR = A / 8;             // 16-byte chunks per K/V row
-    constexpr int NCH = TK * CPR;          // chunks per tile
-    constexpr int CPT = (NCH + 255) / 256; // chunks per thread
     constexpr int KK = A / 16;             // 16-dim MFMA steps of QK^T
     constexpr int DT = (A + 31) / 32;      // 32-dim output tiles
-    constexpr int SPAN = PREFILL_QW * (4 / HPW);
+    constexpr int QW = PREFILL_QW;         // positions per wave (32)
+    constexpr int SPAN = QW * (4 / HPW);   // positions per workgroup
+    constexpr int LOADERS = (TK / 4) * CPR;  // threads that each load 4 keys x 8 dims
     constexpr float NEG_BIG = -1.0e30f;
+    constexpr float RESCALE_SLACK = 8.0f;  // log2 units: weights stay < 2^8
+    static_assert(LOADERS <= 256, "tile loaders");
+    static_assert(BS % 4 == 0, "4 consecutive keys must share a block");
 
-    __shared__ uint4 sK[TK * CPR];          // [key][chunk ^ (key % CPR)]
-    __shared__ uint2 sVt[A * (TK / 4)];     // [dim][keygroup ^ ((dim >> 1) & 15)], 4 keys per uint2
+    __shared__ uint4 sK[2][TK * CPR];       // [key][chunk ^ (key % CPR)]
+    __shared__ uint4 sVt[2][A * (TK / 8)];  // [dim][8-key chunk ^ vswz(dim)]
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int hi = lane >> 5;   // which half of the wave
-    const int col = lane & 31;  // query column inside a 32-wide tile
+    const int col = lane & 31;  // query column of this lane
 
     if ((int)blockIdx.x >= P.hdr[HDR_N_PRE]) return;
     const int2 it = P.items[blockIdx.x];
@@ -87,188 +110,212 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams P) {
     const int qlen = P.cu[s + 1] - row0;
     const int c = P.ctx[s];
     const int L = c + qlen;
-    const int p0 = tile * SPAN + (wave / HPW) * PREFILL_QW;  // first position of this wave
-    const int wg_last = min(tile * SPAN + SPAN, qlen) - 1;     // last position of the workgroup
-    const int kend = c + wg_last + 1;                          // keys the workgroup needs
-    const int nkt = (kend + TK - 1) / TK;
-    const int w_last = min(p0 + PREFILL_QW, qlen) - 1;         // last position of this wave
-    const int kend_w = (p0 < qlen) ? c + w_last + 1 : 0;
+    const int p0 = tile * SPAN + (wave / HPW) * QW;         // first position of this wave
+    const int wg_last = min(tile * SPAN + SPAN, qlen) - 1;  // last position of the workgroup
+    const int nkt = (c + wg_last + 1 + TK - 1) / TK;        // key tiles the workgroup needs
+    const int kend_w = (p0 < qlen) ? c + min(p0 + QW, qlen) : 0;  // keys this wave needs
+    const float cs = P.scale_log2;
+    const bool pos_scale = cs > 0.f;
 
-    // ---- Q^T operand: two 32-column tiles, KK 16-dim steps ----------------
-    uint4 qreg[2][KK];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const int pos = p0 + qt * 32 + col;
+    // ---- Q^T operand: 32 columns, KK 16-dim steps -------------------------
+    uint4 qreg[KK];
+    {
+        const int pos = p0 + col;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            qreg[qt][kk] = make_uint4(0, 0, 0, 0);
+            qreg[kk] = make_uint4(0, 0, 0, 0);
             if (pos < qlen)
-                qreg[qt][kk] = *reinterpret_cast<const uint4*>(
+                qreg[kk] = *reinterpret_cast<const uint4*>(
                     P.q + (((int64_t)(row0 + pos) * P.hq + h) * A + kk * 16 + hi * 8));
         }
     }
 
-    f32x16_t o[2][DT];
+    f32x16_t o[DT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qt][dt][r] = 0.f;
-    float m[2] = {NEG_BIG, NEG_BIG};
-    float lsum[2] = {0.f, 0.f};
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m = NEG_BIG;  // running maximum, scaled log2 units
+    float lsum = 0.f;
 
-    // ---- cooperative tile loads (global -> registers) ---------------------
-    uint4 kreg[CPT], vreg[CPT];
+    // ---- cooperative tile loads: thread = 4 consecutive keys x one chunk ----
+    // Keys at or past L load a copy of row L-1 (same 4-aligned group, so the
+    // same block): their weight is exactly 0 for every row that is stored,
+    // and the copy keeps their values finite.
+    const bool loader = tid < LOADERS;
+    const int kg = tid / CPR;  // key group: keys 4kg .. 4kg+3 of the tile
+    const int cc = tid % CPR;  // 16-byte chunk of the row (dims 8cc .. 8cc+7)
+    // V^T key order: key 16a+8b+4c+e is stored at 16a+8c+4b+e, so the eight
+    // keys a lane feeds to one P.V step (16a+4c+{0..3} and 16a+8+4c+{0..3})
+    // form one 16-byte chunk (2a+c) of the transposed row.
+    const int vunit = 4 * (kg >> 2) + 2 * (kg & 1) + ((kg >> 1) & 1);
+    uint4 kreg[4], vreg[4];
     int bad = 0;
     auto load_tile = [&](int k0) {
+        if (!loader) return;
+        const int key0 = min(k0 + 4 * kg, L - 1);
+        const int lb = key0 / BS;  // the (clamped) 4 keys share one block
+        int64_t blk = 0;
+        if (lb < P.max_blocks) blk = P.table[(int64_t)s * P.max_blocks + lb];
+        if (lb >= P.max_blocks || blk < 0 || blk >= P.num_blocks) {
+            bad = 1;
+            blk = 0;
+        }
+        const int64_t base = ((blk * P.hkv + kvh) * BS + key0 % BS) * CPR + cc;
+        const uint4* kp = P.k_cache + base;
+        const uint4* vp = P.v_cache + base;
+        if (k0 + 4 * kg + 3 < L) {  // whole group in range: constant row offsets
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ci = tid + i * 256;
-            kreg[i] = make_uint4(0, 0, 0, 0);
-            vreg[i] = make_uint4(0, 0, 0, 0);
-            if (ci < NCH) {
-                const int key = ci / CPR, cc = ci % CPR;
-                const int kidx = k0 + key;
-                if (kidx < L) {
-                    const int lb = kidx / BS;
-                    int64_t blk = -1;
-                    if (lb < P.max_blocks) blk = P.table[(int64_t)s * P.max_blocks + lb];
-                    if (blk >= 0 && blk < P.num_blocks) {
-                        const int64_t off = ((blk * P.hkv + kvh) * BS + kidx % BS) * CPR + cc;
-                        kreg[i] = P.k_cache[off];
-                        vreg[i] = P.v_cache[off];
-                    } else {
-                        bad = 1;
-                    }
-                }
+            for (int j = 0; j < 4; ++j) {
+                kreg[j] = kp[j * CPR];
+                vreg[j] = vp[j * CPR];
+            }
+        } else {  // the sequence's last keys: rows past L repeat row L-1
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int dj = min(k0 + 4 * kg + j, L - 1) - key0;
+                kreg[j] = kp[dj * CPR];
+                vreg[j] = vp[dj * CPR];
             }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
+        if (!loader) return;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int ci = tid + i * 256;
-            if (ci < NCH) {
-                const int key = ci / CPR, cc = ci % CPR;
-                sK[key * CPR + (cc ^ (key % CPR))] = kreg[i];
-                const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-                uint16_t* vt = reinterpret_cast<uint16_t*>(sVt);
+        for (int j = 0; j < 4; ++j) {
+            const int key = 4 * kg + j;
+            sK[buf][key * CPR + (cc ^ (key % CPR))] = kreg[j];
+        }
+        const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+        const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+        const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
+        const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+        uint2* vt = reinterpret_cast<uint2*>(&sVt[buf][0]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = cc * 8 + e;
-                    const int unit = (key >> 2) ^ ((d >> 1) & 15);
-                    const uint16_t val = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
-                    vt[(d * (TK / 4) + unit) * 4 + (key & 3)] = val;
-                }
+        for (int e = 0; e < 8; ++e) {
+            const int d = cc * 8 + e;
+            const int w = e >> 1;
+            uint2 v;
+            if (e & 1) {
+                v.x = pack_hi(w0[w], w1[w]);
+                v.y = pack_hi(w2[w], w3[w]);
+            } else {
+                v.x = pack_lo(w0[w], w1[w]);
+                v.y = pack_lo(w2[w], w3[w]);
             }
+            const int chunk = (vunit >> 1) ^ vswz(d);
+            vt[(d * (TK / 8) + chunk) * 2 + (vunit & 1)] = v;
         }
     };
 
-    if (nkt > 0) load_tile(0);
+    if (nkt > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
     for (int t = 0; t < nkt; ++t) {
         const int k0 = t * TK;
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (t + 1 < nkt) load_tile(k0 + TK);
-        if (k0 >= kend_w) continue;  // this wave's rows see no key of the tile
+        const int buf = t & 1;
+        if (t + 1 < nkt) load_tile(k0 + TK);  // in flight during this tile's math
 
-        // ---- S^T = K Q^T : 2 key halves x 2 query tiles -----------------
-        f32x16_t sacc[2][2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        if (k0 < kend_w) {
+            // ---- S^T = K Q^T : two 32-key halves -------------------------
+            f32x16_t sacc[2];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[qt][kh][r] = 0.f;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const int key = kh * 32 + col;
+                for (int r = 0; r < 16; ++r) sacc[kh][r] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const int cc = kk * 2 + hi;
-                const uint4 a = sK[key * CPR + (cc ^ (key % CPR))];
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) sacc[qt][kh] = mfma32(a, qreg[qt][kk], sacc[qt][kh]);
+                for (int kh = 0; kh < 2; ++kh) {
+                    const int key = kh * 32 + col;
+                    const int ch = kk * 2 + hi;
+                    const uint4 a = sK[buf][key * CPR + (ch ^ (key % CPR))];
+                    sacc[kh] = mfma32(a, qreg[kk], sacc[kh]);
+                }
             }
-        }
 
-        // ---- online softmax per query column ----------------------------
-        const bool diag = k0 + TK - 1 > c + p0;  // some key of the tile may be masked
-        uint4 pb[2][2][2];  // [qt][kh][ks] bf16 P^T operands
+            // ---- online softmax of this lane's column ---------------------
+            const int lim = c + p0 + col;               // last visible key of the column
+            const bool diag = k0 + TK - 1 > c + p0;     // some key may be masked
+            if (!pos_scale) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const int pos = p0 + qt * 32 + col;
-            const int lim = c + pos;  // last visible key
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[kh][r] *= cs;
+            }
+            if (diag) {
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + kh * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        if (key > lim) sacc[kh][r] = -INFINITY;
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kh * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    float v = sacc[qt][kh][r] * P.scale_log2;
-                    if (diag && key > lim) v = -INFINITY;
-                    sacc[qt][kh][r] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kh][r]);
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
-            const float m_new = fmaxf(m[qt], mx);
-            const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
-            m[qt] = m_new;
-            float ps = 0.f;
+            const float cand = pos_scale ? mx * cs : mx;  // column max, scaled log2 units
+            const bool grow = cand > m + RESCALE_SLACK;
+            if (__any(grow)) {
+                const float m_new = grow ? cand : m;
+                const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+                m = m_new;
+                lsum *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            }
+            const float mc = pos_scale ? cs : 1.f;
+            uint4 pb[2][2];  // [kh][ks] bf16 P^T operands
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 float p[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    p[r] = __builtin_amdgcn_exp2f(sacc[qt][kh][r] - m_new);
-                    ps += p[r];
+                    p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][r], mc, -m));
+                    lsum += p[r];
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    pb[qt][kh][ks].x = pack_bf16x2(p[ks * 8 + 0], p[ks * 8 + 1]);
-                    pb[qt][kh][ks].y = pack_bf16x2(p[ks * 8 + 2], p[ks * 8 + 3]);
-                    pb[qt][kh][ks].z = pack_bf16x2(p[ks * 8 + 4], p[ks * 8 + 5]);
-                    pb[qt][kh][ks].w = pack_bf16x2(p[ks * 8 + 6], p[ks * 8 + 7]);
+                    pb[kh][ks].x = pack_bf16x2(p[ks * 8 + 0], p[ks * 8 + 1]);
+                    pb[kh][ks].y = pack_bf16x2(p[ks * 8 + 2], p[ks * 8 + 3]);
+                    pb[kh][ks].z = pack_bf16x2(p[ks * 8 + 4], p[ks * 8 + 5]);
+                    pb[kh][ks].w = pack_bf16x2(p[ks * 8 + 6], p[ks * 8 + 7]);
                 }
             }
-            lsum[qt] = lsum[qt] * alpha + ps;
+
+            // ---- O^T += V^T P^T ---------------------------------------------
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = dt * 32 + col;
+                const int sw = vswz(d);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[qt][dt][r] *= alpha;
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        uint4 a = make_uint4(0, 0, 0, 0);
+                        if (d < A) a = sVt[buf][d * (TK / 8) + ((2 * (2 * kh + ks) + hi) ^ sw)];
+                        o[dt] = mfma32(a, pb[kh][ks], o[dt]);
+                    }
+            }
         }
 
-        // ---- O^T += V^T P^T ----------------------------------------------
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int d = dt * 32 + col;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    uint4 a = make_uint4(0, 0, 0, 0);
-                    if (d < A) {
-                        const int base = kh * 32 + ks * 16 + hi * 4;  // keys base..base+3, base+8..+11
-                        const int sw = (d >> 1) & 15;
-                        const uint2 lo = sVt[d * (TK / 4) + ((base >> 2) ^ sw)];
-                        const uint2 hi2 = sVt[d * (TK / 4) + (((base + 8) >> 2) ^ sw)];
-                        a = make_uint4(lo.x, lo.y, hi2.x, hi2.y);
-                    }
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) o[qt][dt] = mfma32(a, pb[qt][kh][ks], o[qt][dt]);
-                }
-        }
+        if (t + 1 < nkt) store_tile(buf ^ 1);
+        __syncthreads();
     }
-    if (bad) atomicOr(const_cast<int32_t*>(P.hdr) + HDR_FLAGS, FLAG_BAD_BLOCK);
+    if (bad) atomicOr(P.hdr + HDR_FLAGS, FLAG_BAD_BLOCK);
 
     // ---- normalise and store ------------------------------------------------
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const int pos = p0 + qt * 32 + col;
-        const float lt = lsum[qt] + shfl_xor_f(lsum[qt], 32);
-        if (pos >= qlen) continue;
+    const int pos = p0 + col;
+    const float lt = lsum + shfl_xor_f(lsum, 32);
+    if (pos < qlen) {
         const float inv = 1.f / lt;
         uint16_t* orow = P.out + ((int64_t)(row0 + pos) * P.hq + h) * A;
 #pragma unroll
@@ -278,8 +325,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams P) {
                 const int d = dt * 32 + 8 * rg + 4 * hi;
                 if (d < A) {
                     uint2 v;
-                    v.x = pack_bf16x2(o[qt][dt][rg * 4 + 0] * inv, o[qt][dt][rg * 4 + 1] * inv);
-                    v.y = pack_bf16x2(o[qt][dt][rg * 4 + 2] * inv, o[qt][dt][rg * 4 + 3] * inv);
+                    v.x = pack_bf16x2(o[dt][rg * 4 + 0] * inv, o[dt][rg * 4 + 1] * inv);
+                    v.y = pack_bf16x2(o[dt][rg * 4 + 2] * inv, o[dt][rg * 4 + 3] * inv);
                     *reinterpret_cast<uint2*>(orow + d) = v;
                 }
             }
@@ -310,8 +357,8 @@ hipError_t launch_prefill(const StepArgs& a) {
     p.table = a.block_table;
     p.cu = a.cu_seqlens_q;
     p.ctx = a.context_lens;
-    p.hdr = (const int32_t*)(ws + a.lay.hdr);
-    p.items = (const int2*)(ws + a.lay.pre_items);
+    p.hdr = (int32_t*)(ws + a.lay.hdr);
+    p.items = (const int2*)(ws + a.lay.pre_sorted);
     p.num_blocks = a.num_blocks;
     p.max_blocks = a.max_blocks;
     p.hq = a.num_q_heads;
@@ -321,6 +368,7 @@ hipError_t launch_prefill(const StepArgs& a) {
     p.scale_log2 = a.scale * 1.4426950408889634f;
     const int64_t gx = a.lay.cap_pre;
     if (gx <= 0) return hipSuccess;
+    if (gx > INT32_MAX) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx, (unsigned)(a.num_kv_heads * p.HC));
     if (a.head_dim == 128) {
         if (a.block_size == 16) launch_prefill_hpw<128, 16>(a, p, hpw, grid);

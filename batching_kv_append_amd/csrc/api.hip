@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kvc.h"
@@ -112,18 +113,57 @@ int debug_check(const int32_t* cu_d, const int32_t* ctx_d, const int32_t* table_
     return KVC_OK;
 }
 
-// Optional per-kernel timing: HIP events recorded around each launch of
-// kvc_paged_attention_varlen on the caller's stream (kvc_profile_begin/end).
+// Optional per-kernel timing: a start and an end HIP event around each kernel
+// of kvc_paged_attention_varlen, recorded on the stream that kernel runs on
+// (kvc_profile_begin/end).
 struct Profiler {
     bool on = false;
     int32_t max_calls = 0, calls = 0;
-    std::vector<hipEvent_t> ev;  // (KVC_PROF_PHASES + 1) per call
+    std::vector<hipEvent_t> ev;  // 2 * KVC_PROF_PHASES per call: (start, end) per phase
+    std::vector<uint8_t> used;   // per call and phase: both events recorded
 };
 Profiler g_prof;
+std::mutex g_prof_mu;
 
-void prof_mark(int phase, hipStream_t st) {
+void prof_mark(int phase, bool end, hipStream_t st) {
     if (!g_prof.on || g_prof.calls >= g_prof.max_calls) return;
-    hipEventRecord(g_prof.ev[(size_t)g_prof.calls * (KVC_PROF_PHASES + 1) + phase], st);
+    const size_t base = (size_t)g_prof.calls * KVC_PROF_PHASES + phase;
+    hipEventRecord(g_prof.ev[base * 2 + (end ? 1 : 0)], st);
+    if (end) g_prof.used[base] = 1;
+}
+
+// Side stream per device for the prefill kernel, so the matrix-bound prefill
+// overlaps the memory-bound decode.  The call forks to it with an event after
+// the append and joins it with another before returning, so the caller's
+// stream still sees one ordered step.  Created once per device (default
+// priority, non-blocking); a mutex keeps the fork/join event pair of
+// concurrent callers apart.
+struct SideStream {
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[64];
+
+SideStream* side_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideStream& ss = g_side[dev];
+    std::lock_guard<std::mutex> lk(ss.mu);
+    if (!ss.ready) {
+        if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+            return nullptr;
+        ss.ready = true;
+    }
+    return &ss;
+}
+
+bool overlap_enabled() {
+    const char* e = std::getenv("KVC_SERIAL");  // 1: run every kernel on the caller's stream
+    return !(e && e[0] && e[0] != '0');
 }
 
 }  // namespace
@@ -131,9 +171,11 @@ void prof_mark(int phase, hipStream_t st) {
 extern "C" int kvc_profile_begin(int32_t max_calls) {
     if (max_calls < 1 || max_calls > 100000)
         return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_profile_begin: max_calls out of range");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
     g_prof = Profiler{};
-    g_prof.ev.resize((size_t)max_calls * (KVC_PROF_PHASES + 1));
+    g_prof.ev.resize((size_t)max_calls * KVC_PROF_PHASES * 2);
+    g_prof.used.assign((size_t)max_calls * KVC_PROF_PHASES, 0);
     for (auto& e : g_prof.ev) {
         hipError_t r = hipEventCreate(&e);
         if (r != hipSuccess) return hip_fail(r, "kvc_profile_begin");
@@ -145,22 +187,21 @@ extern "C" int kvc_profile_begin(int32_t max_calls) {
 
 extern "C" int kvc_profile_end(double* ms_sum, int32_t* calls) {
     if (!ms_sum || !calls) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_profile_end: NULL pointer");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     for (int p = 0; p < KVC_PROF_PHASES; ++p) ms_sum[p] = 0.0;
     *calls = 0;
-    if (!g_prof.ev.empty()) {
-        for (int32_t c = 0; c < g_prof.calls; ++c) {
-            hipEvent_t* e = &g_prof.ev[(size_t)c * (KVC_PROF_PHASES + 1)];
-            hipError_t r = hipEventSynchronize(e[KVC_PROF_PHASES]);
+    for (int32_t c = 0; c < g_prof.calls; ++c) {
+        for (int p = 0; p < KVC_PROF_PHASES; ++p) {
+            const size_t base = (size_t)c * KVC_PROF_PHASES + p;
+            if (!g_prof.used[base]) continue;
+            hipError_t r = hipEventSynchronize(g_prof.ev[base * 2 + 1]);
+            float ms = 0.f;
+            if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_prof.ev[base * 2], g_prof.ev[base * 2 + 1]);
             if (r != hipSuccess) return hip_fail(r, "kvc_profile_end");
-            for (int p = 0; p < KVC_PROF_PHASES; ++p) {
-                float ms = 0.f;
-                r = hipEventElapsedTime(&ms, e[p], e[p + 1]);
-                if (r != hipSuccess) return hip_fail(r, "kvc_profile_end");
-                ms_sum[p] += ms;
-            }
+            ms_sum[p] += ms;
         }
-        *calls = g_prof.calls;
     }
+    *calls = g_prof.calls;
     for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
     g_prof = Profiler{};
     return KVC_OK;
@@ -299,21 +340,47 @@ extern "C" int kvc_paged_attention_varlen(
     a.lay = lay;
     a.stream = st;
 
-    prof_mark(KVC_PROF_PLAN, st);
+    std::unique_lock<std::mutex> prof_lk(g_prof_mu);
+    prof_mark(KVC_PROF_PLAN, false, st);
     hipError_t e = kvc::launch_plan(a);
-    prof_mark(KVC_PROF_APPEND, st);
-    if (e == hipSuccess && k_new)
+    prof_mark(KVC_PROF_PLAN, true, st);
+    if (e == hipSuccess && k_new) {
+        prof_mark(KVC_PROF_APPEND, false, st);
         e = kvc::launch_append(k_new, v_new, k_cache, v_cache, num_blocks, block_table,
                                max_blocks_per_seq, cu_seqlens_q, context_lens, num_seqs, total_q,
                                num_kv_heads, head_dim, block_size,
                                (int32_t*)((char*)workspace + lay.hdr), st);
-    prof_mark(KVC_PROF_PREFILL, st);
-    if (e == hipSuccess) e = kvc::launch_prefill(a);
-    prof_mark(KVC_PROF_DECODE, st);
+        prof_mark(KVC_PROF_APPEND, true, st);
+    }
+    // The prefill kernel (rows of chunks with >= 2 new tokens) runs on the side
+    // stream when there is one, concurrently with decode and merge.
+    SideStream* ss = (max_q_len >= 2 && overlap_enabled()) ? side_stream() : nullptr;
+    std::unique_lock<std::mutex> side_lk;
+    if (ss) side_lk = std::unique_lock<std::mutex>(ss->mu);
+    if (e == hipSuccess && max_q_len >= 2) {
+        kvc::StepArgs ap = a;
+        if (ss) {
+            e = hipEventRecord(ss->fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+            ap.stream = ss->stream;
+        }
+        prof_mark(KVC_PROF_PREFILL, false, ap.stream);
+        if (e == hipSuccess) e = kvc::launch_prefill(ap);
+        prof_mark(KVC_PROF_PREFILL, true, ap.stream);
+        if (ss && e == hipSuccess) e = hipEventRecord(ss->join, ss->stream);
+    }
+    prof_mark(KVC_PROF_DECODE, false, st);
     if (e == hipSuccess) e = kvc::launch_decode(a);
-    prof_mark(KVC_PROF_MERGE, st);
+    prof_mark(KVC_PROF_DECODE, true, st);
+    prof_mark(KVC_PROF_MERGE, false, st);
     if (e == hipSuccess) e = kvc::launch_merge(a);
-    prof_mark(KVC_PROF_PHASES, st);
+    prof_mark(KVC_PROF_MERGE, true, st);
+    if (ss && max_q_len >= 2) {
+        // join even after a failed launch, so the caller's stream never runs
+        // ahead of work already queued on the side stream
+        hipError_t ej = hipStreamWaitEvent(st, ss->join, 0);
+        if (e == hipSuccess) e = ej;
+    }
     if (g_prof.on && g_prof.calls < g_prof.max_calls) ++g_prof.calls;
     return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
 }

@@ -47,7 +47,13 @@
  *             block_table[s][p / block_size], slot p % block_size.
  *   Heads     Query head h reads kv head h / (num_q_heads / num_kv_heads).
  *   Streams   `stream` is a hipStream_t (NULL = the null stream).  Device
- *             work is enqueued asynchronously, in stream order.
+ *             work is enqueued asynchronously, in stream order.  When a step
+ *             has prefill chunks, kvc_paged_attention_varlen runs the prefill
+ *             kernel on one internal side stream per device (created on first
+ *             use, default priority), forked from `stream` after the append
+ *             and joined back before the call returns, so it overlaps the
+ *             decode kernels; to the caller the step is still one ordered
+ *             piece of `stream`.  KVC_SERIAL=1 keeps every kernel on `stream`.
  *   Errors    Every entry point returns a kvc_status.  Arguments are checked
  *             before anything is enqueued, so a call that returns an error
  *             has had no effect.  Values inside device arrays (table entries,
@@ -204,13 +210,13 @@ int kvc_workspace_flags(const void* workspace, void* stream, int32_t* flags);
 /* ------------------------------------------------------------------------
  * Optional per-kernel timing (instrumentation; off by default).
  * kvc_profile_begin(n) makes the next n calls of kvc_paged_attention_varlen
- * record a HIP event before each of its kernels and one after the last, on
- * the call's stream (host-side hipEventCreate only; no device memory).
- * kvc_profile_end waits for those events, writes into ms_sum[KVC_PROF_PHASES]
- * the summed milliseconds between consecutive events (phase p = from the
- * event before kernel p to the one before kernel p+1; a phase whose kernel
- * was not needed reads about 0), writes the number of recorded calls, and
- * turns timing off.  Not thread-safe: one profiling client at a time.
+ * record a HIP event just before and just after each of its kernels, on the
+ * stream that kernel runs on (host-side hipEventCreate only; no device
+ * memory).  kvc_profile_end waits for those events, writes into
+ * ms_sum[KVC_PROF_PHASES] the summed start-to-end milliseconds of each kernel
+ * over the recorded calls (0 for a kernel a call did not need), writes the
+ * number of recorded calls, and turns timing off.  One profiling client at a
+ * time.
  * ---------------------------------------------------------------------- */
 enum {
     KVC_PROF_PLAN = 0,    /* work-list planning                      */

@@ -341,17 +341,10 @@ extern "C" int kvc_paged_attention_varlen(
     a.stream = st;
 
     std::unique_lock<std::mutex> prof_lk(g_prof_mu);
+    // planning and append share one launch (counted under "plan")
     prof_mark(KVC_PROF_PLAN, false, st);
-    hipError_t e = kvc::launch_plan(a);
+    hipError_t e = kvc::launch_prep(a, k_new != nullptr);
     prof_mark(KVC_PROF_PLAN, true, st);
-    if (e == hipSuccess && k_new) {
-        prof_mark(KVC_PROF_APPEND, false, st);
-        e = kvc::launch_append(k_new, v_new, k_cache, v_cache, num_blocks, block_table,
-                               max_blocks_per_seq, cu_seqlens_q, context_lens, num_seqs, total_q,
-                               num_kv_heads, head_dim, block_size,
-                               (int32_t*)((char*)workspace + lay.hdr), st);
-        prof_mark(KVC_PROF_APPEND, true, st);
-    }
     // The prefill kernel (rows of chunks with >= 2 new tokens) runs on the side
     // stream when there is one, concurrently with decode and merge.
     SideStream* ss = (max_q_len >= 2 && overlap_enabled()) ? side_stream() : nullptr;

@@ -28,28 +28,9 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int64_t t = (int64_t)blockIdx.x * ROWS_PER_WG + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= total_q) return;
-    const int s = find_seq(cu, num_seqs, t);
-    const int64_t p = (int64_t)ctx[s] + (t - cu[s]);
-    const int64_t lb = p / block_size;
-    if (p < 0 || lb >= max_blocks) {
-        if (hdr && lane == 0) set_flag(hdr, FLAG_TABLE_SHORT);
-        return;
-    }
-    const int64_t blk = table[(int64_t)s * max_blocks + lb];
-    if (blk < 0 || blk >= num_blocks) {
-        if (hdr && lane == 0) set_flag(hdr, FLAG_BAD_BLOCK);
-        return;
-    }
-    const int slot = (int)(p % block_size);
-    const int cpr = head_dim >> 3;  // 16-byte chunks per head row
-    const int nchunk = hkv * cpr;
-    for (int c = lane; c < nchunk; c += 64) {
-        const int g = c / cpr, e = c - g * cpr;
-        const int64_t dst = ((blk * hkv + g) * block_size + slot) * cpr + e;
-        const int64_t src = (t * hkv + g) * cpr + e;
-        k_cache[dst] = k_new[src];
-        v_cache[dst] = v_new[src];
-    }
+    const int f = append_row(k_new, v_new, k_cache, v_cache, num_blocks, table, max_blocks, cu, ctx,
+                             num_seqs, t, hkv, head_dim, block_size, lane);
+    if (f && hdr && lane == 0) set_flag(hdr, f);
 }
 
 __global__ __launch_bounds__(256) void gather_kernel(

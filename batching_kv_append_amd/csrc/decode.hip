@@ -38,11 +38,50 @@ constexpr int PLAN_THREADS = 1024;
 
 constexpr int COST_BUCKETS = 1024;  // prefill cost histogram (key tiles, clamped)
 
-__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ ctx, int32_t num_seqs,
-    int32_t total_q, int32_t max_q_len, int32_t max_context_len, int32_t span, int64_t cap_dec,
-    int64_t cap_pre, int32_t* hdr, int32_t* dec_base, int2* dec_items, int2* pre_items,
-    int2* pre_sorted, int32_t* merge_list) {
+struct PrepParams {
+    // planning
+    const int32_t* cu;
+    const int32_t* ctx;
+    int32_t num_seqs, total_q, max_q_len, max_context_len, span;
+    int64_t cap_dec, cap_pre;
+    int32_t* hdr;
+    int32_t* dec_base;
+    int2* dec_items;
+    int2* pre_items;
+    int2* pre_sorted;
+    int32_t* merge_list;
+    // append (k_new == nullptr: nothing to append)
+    const uint4* k_new;
+    const uint4* v_new;
+    uint4* k_cache;
+    uint4* v_cache;
+    int64_t num_blocks;
+    const int32_t* table;
+    int32_t max_blocks, hkv, head_dim, block_size;
+};
+
+// Workgroup 0 plans; workgroups 1.. append the new rows (one wave per row).
+// Only the planner writes the flag word (it zeroes it first): it also checks
+// the table entries the append will use, and the append skips bad entries.
+__global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
+    if (blockIdx.x > 0) {
+        const int64_t t = (int64_t)(blockIdx.x - 1) * (PLAN_THREADS / 64) + (threadIdx.x >> 6);
+        if (P.k_new == nullptr || t >= P.total_q) return;
+        append_row(P.k_new, P.v_new, P.k_cache, P.v_cache, P.num_blocks, P.table, P.max_blocks,
+                   P.cu, P.ctx, P.num_seqs, t, P.hkv, P.head_dim, P.block_size, threadIdx.x & 63);
+        return;
+    }
+    const int32_t* __restrict__ cu = P.cu;
+    const int32_t* __restrict__ ctx = P.ctx;
+    const int32_t num_seqs = P.num_seqs, total_q = P.total_q, max_q_len = P.max_q_len;
+    const int32_t max_context_len = P.max_context_len, span = P.span;
+    const int64_t cap_dec = P.cap_dec, cap_pre = P.cap_pre;
+    int32_t* hdr = P.hdr;
+    int32_t* dec_base = P.dec_base;
+    int2* dec_items = P.dec_items;
+    int2* pre_items = P.pre_items;
+    int2* pre_sorted = P.pre_sorted;
+    int32_t* merge_list = P.merge_list;
     __shared__ int sc[3][PLAN_THREADS];
     __shared__ int hist[COST_BUCKETS];
     __shared__ int carry[3];
@@ -77,6 +116,16 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(
                 nm = nd > 1;
             } else if (q >= 2) {
                 np = (q + span - 1) / span;
+            }
+            if (P.k_new != nullptr && r1 > r0 && r0 >= 0 && r1 <= total_q && c >= 0) {
+                // blocks holding positions c .. c + (r1 - r0) - 1 (the append's targets)
+                const int64_t lb_lo = c / P.block_size;
+                const int64_t lb_hi = ((int64_t)c + (r1 - r0) - 1) / P.block_size;
+                for (int64_t lb = lb_lo; lb <= lb_hi; ++lb) {
+                    if (lb >= P.max_blocks) { atomicOr(&flags, FLAG_TABLE_SHORT); break; }
+                    const int32_t id = P.table[(int64_t)s * P.max_blocks + lb];
+                    if (id < 0 || id >= P.num_blocks) atomicOr(&flags, FLAG_BAD_BLOCK);
+                }
             }
         }
         sc[0][tid] = nd;
@@ -661,19 +710,37 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
     const int np = (L + DECODE_PART - 1) / DECODE_PART;
     const int64_t base = P.dec_base[s];
     if (base < 0 || base + np > P.cap_dec) return;  // never true for a planned sequence
-    float M = NEG_BIG;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, P.ws_ml[((base + p) * P.hq + h) * 2]);
-    float den = 0.f, num[DPL];
+    const int d0 = lane * DPL;
+    float M = NEG_BIG, den = 0.f, num[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) num[i] = 0.f;
-    const int d0 = lane * DPL;
-    for (int p = 0; p < np; ++p) {
-        const int64_t slot = (base + p) * P.hq + h;
-        const float w = __builtin_amdgcn_exp2f(P.ws_ml[slot * 2] - M);
-        den = fmaf(w, P.ws_ml[slot * 2 + 1], den);
-        if (d0 < A) {
+    // Partitions in groups of 64: lane p holds partition p's (m, l); every
+    // lane streams the accumulators of all partitions for its dims.
+    for (int c0 = 0; c0 < np; c0 += 64) {
+        const int n = min(64, np - c0);
+        const int pi = min(lane, n - 1);
+        const float2 ml = *reinterpret_cast<const float2*>(P.ws_ml + ((base + c0 + pi) * P.hq + h) * 2);
+        const float mp = lane < n ? ml.x : NEG_BIG;
+        float cm = mp;
 #pragma unroll
-            for (int i = 0; i < DPL; ++i) num[i] = fmaf(w, P.ws_acc[slot * A + d0 + i], num[i]);
+        for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, shfl_xor_f(cm, off));
+        const float Mn = fmaxf(M, cm);
+        const float a = __builtin_amdgcn_exp2f(M - Mn);
+        den *= a;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) num[i] *= a;
+        M = Mn;
+        const float w = lane < n ? __builtin_amdgcn_exp2f(mp - M) : 0.f;
+        float wl = lane < n ? w * ml.y : 0.f;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) wl += shfl_xor_f(wl, off);
+        den += wl;
+        const float* accp = P.ws_acc + ((base + c0) * P.hq + h) * A + min(d0, A - DPL);
+#pragma unroll 8
+        for (int p = 0; p < n; ++p) {
+            const float wp = __shfl(w, p, 64);
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) num[i] = fmaf(wp, accp[(int64_t)p * P.hq * A + i], num[i]);
         }
     }
     if (d0 < A) {
@@ -715,15 +782,38 @@ int decode_heads_per_wave(int G, int head_dim) {
     return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
-hipError_t launch_plan(const StepArgs& a) {
+hipError_t launch_prep(const StepArgs& a, bool with_append) {
     char* ws = a.ws;
     const int G = a.num_q_heads / a.num_kv_heads;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, a.stream, a.cu_seqlens_q,
-                       a.context_lens, a.num_seqs, a.total_q, a.max_q_len, a.max_context_len,
-                       prefill_span(G), a.lay.cap_dec, a.lay.cap_pre,
-                       (int32_t*)(ws + a.lay.hdr), (int32_t*)(ws + a.lay.dec_base),
-                       (int2*)(ws + a.lay.dec_items), (int2*)(ws + a.lay.pre_items),
-                       (int2*)(ws + a.lay.pre_sorted), (int32_t*)(ws + a.lay.merge_list));
+    PrepParams p;
+    p.cu = a.cu_seqlens_q;
+    p.ctx = a.context_lens;
+    p.num_seqs = a.num_seqs;
+    p.total_q = a.total_q;
+    p.max_q_len = a.max_q_len;
+    p.max_context_len = a.max_context_len;
+    p.span = prefill_span(G);
+    p.cap_dec = a.lay.cap_dec;
+    p.cap_pre = a.lay.cap_pre;
+    p.hdr = (int32_t*)(ws + a.lay.hdr);
+    p.dec_base = (int32_t*)(ws + a.lay.dec_base);
+    p.dec_items = (int2*)(ws + a.lay.dec_items);
+    p.pre_items = (int2*)(ws + a.lay.pre_items);
+    p.pre_sorted = (int2*)(ws + a.lay.pre_sorted);
+    p.merge_list = (int32_t*)(ws + a.lay.merge_list);
+    p.k_new = with_append ? (const uint4*)a.k_new : nullptr;
+    p.v_new = with_append ? (const uint4*)a.v_new : nullptr;
+    p.k_cache = (uint4*)a.k_cache;
+    p.v_cache = (uint4*)a.v_cache;
+    p.num_blocks = a.num_blocks;
+    p.table = a.block_table;
+    p.max_blocks = a.max_blocks;
+    p.hkv = a.num_kv_heads;
+    p.head_dim = a.head_dim;
+    p.block_size = a.block_size;
+    const int64_t rows_per_wg = PLAN_THREADS / 64;
+    const int64_t grid = 1 + (with_append ? ((int64_t)a.total_q + rows_per_wg - 1) / rows_per_wg : 0);
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(PLAN_THREADS), 0, a.stream, p);
     return hipGetLastError();
 }
 

@@ -116,6 +116,36 @@ __device__ __forceinline__ int find_seq(const T* cu, int num_seqs, int64_t t) {
     }
     return lo;
 }
+// Copy the K and V rows of new token t (kv heads x head_dim bf16, 16-byte
+// chunks spread over the 64 lanes of the calling wave) into the pool slot of
+// its position context_lens[s] + (t - cu[s]).  A position outside the table
+// or a block id outside [0, num_blocks) is skipped: the return value is
+// FLAG_TABLE_SHORT / FLAG_BAD_BLOCK (0 when the row was written).
+__device__ __forceinline__ int append_row(const uint4* __restrict__ k_new,
+                                          const uint4* __restrict__ v_new, uint4* __restrict__ k_cache,
+                                          uint4* __restrict__ v_cache, int64_t num_blocks,
+                                          const int32_t* __restrict__ table, int32_t max_blocks,
+                                          const int32_t* __restrict__ cu, const int32_t* __restrict__ ctx,
+                                          int32_t num_seqs, int64_t t, int32_t hkv, int32_t head_dim,
+                                          int32_t block_size, int lane) {
+    const int s = find_seq(cu, num_seqs, t);
+    const int64_t p = (int64_t)ctx[s] + (t - cu[s]);
+    const int64_t lb = p / block_size;
+    if (p < 0 || lb >= max_blocks) return FLAG_TABLE_SHORT;
+    const int64_t blk = table[(int64_t)s * max_blocks + lb];
+    if (blk < 0 || blk >= num_blocks) return FLAG_BAD_BLOCK;
+    const int slot = (int)(p % block_size);
+    const int cpr = head_dim >> 3;  // 16-byte chunks per head row
+    const int nchunk = hkv * cpr;
+    for (int c = lane; c < nchunk; c += 64) {
+        const int g = c / cpr, e = c - g * cpr;
+        const int64_t dst = ((blk * hkv + g) * block_size + slot) * cpr + e;
+        const int64_t src = (t * hkv + g) * cpr + e;
+        k_cache[dst] = k_new[src];
+        v_cache[dst] = v_new[src];
+    }
+    return 0;
+}
 #endif  // __HIPCC__
 
 }  // namespace kvc

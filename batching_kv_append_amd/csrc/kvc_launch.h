@@ -41,8 +41,9 @@ hipError_t launch_gather(const void* k_cache, const void* v_cache, int64_t num_b
                          void* v_out, int32_t num_seqs, int32_t hkv, int32_t head_dim,
                          int32_t block_size, hipStream_t stream);
 
-// Work lists for the decode and prefill kernels (zeroes the header flags).
-hipError_t launch_plan(const StepArgs& a);
+// One launch: work lists for the decode and prefill kernels (zeroes the
+// header flags) and, with_append, the append of k_new / v_new.
+hipError_t launch_prep(const StepArgs& a, bool with_append);
 // Split-K decode partials (+ direct output for one-partition sequences).
 hipError_t launch_decode(const StepArgs& a);
 // Log-sum-exp merge of the partials of multi-partition decode sequences.

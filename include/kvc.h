@@ -219,8 +219,8 @@ int kvc_workspace_flags(const void* workspace, void* stream, int32_t* flags);
  * time.
  * ---------------------------------------------------------------------- */
 enum {
-    KVC_PROF_PLAN = 0,    /* work-list planning                      */
-    KVC_PROF_APPEND = 1,  /* kv_append                               */
+    KVC_PROF_PLAN = 0,    /* work-list planning + append (one launch) */
+    KVC_PROF_APPEND = 1,  /* reserved: the append shares the plan launch */
     KVC_PROF_PREFILL = 2, /* MFMA prefill-chunk kernel               */
     KVC_PROF_DECODE = 3,  /* split-K decode partials                 */
     KVC_PROF_MERGE = 4,   /* log-sum-exp merge of decode partials    */

@@ -45,11 +45,10 @@ struct PrepParams {
     int32_t num_seqs, total_q, max_q_len, max_context_len, span;
     int64_t cap_dec, cap_pre;
     int32_t* hdr;
-    int32_t* dec_base;
     int2* dec_items;
     int2* pre_items;
     int2* pre_sorted;
-    int32_t* merge_list;
+    int4* merge_list;  // (sequence, first item, partitions, output row)
     // append (k_new == nullptr: nothing to append)
     const uint4* k_new;
     const uint4* v_new;
@@ -77,11 +76,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     const int32_t max_context_len = P.max_context_len, span = P.span;
     const int64_t cap_dec = P.cap_dec, cap_pre = P.cap_pre;
     int32_t* hdr = P.hdr;
-    int32_t* dec_base = P.dec_base;
     int2* dec_items = P.dec_items;
     int2* pre_items = P.pre_items;
     int2* pre_sorted = P.pre_sorted;
-    int32_t* merge_list = P.merge_list;
+    int4* merge_list = P.merge_list;
     __shared__ int sc[3][PLAN_THREADS];
     __shared__ int hist[COST_BUCKETS];
     __shared__ int carry[3];
@@ -95,9 +93,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     __syncthreads();
     for (int base = 0; base < num_seqs; base += PLAN_THREADS) {
         const int s = base + tid;
-        int nd = 0, np = 0, nm = 0, q = 0;
+        int nd = 0, np = 0, nm = 0, q = 0, row0 = 0;
         if (s < num_seqs) {
             const int r0 = cu[s], r1 = cu[s + 1];
+            row0 = r0;
             const int c = ctx[s];
             q = r1 - r0;
             // A sequence whose rows are not inside [0, total_q) or whose
@@ -150,7 +149,6 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
         const int op = carry[1] + sc[1][tid] - np;
         const int om = carry[2] + sc[2][tid] - nm;
         if (s < num_seqs) {
-            dec_base[s] = q == 1 ? od : -1;
             for (int j = 0; j < nd; ++j) {
                 if (od + j < cap_dec) dec_items[od + j] = make_int2(s, j);
                 else atomicOr(&flags, FLAG_CAPACITY);
@@ -160,7 +158,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
                 if (op + j < cap_pre) pre_items[op + j] = make_int2(s, np - 1 - j);
                 else atomicOr(&flags, FLAG_CAPACITY);
             }
-            if (nm) merge_list[om] = s;
+            if (nm) merge_list[om] = make_int4(s, od, nd, row0);
         }
         __syncthreads();
         if (tid == PLAN_THREADS - 1) {
@@ -683,45 +681,65 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
 // ---------------------------------------------------------------------------
 // Merge kernel: one wave per (multi-partition decode sequence, query head).
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
+// The plan's descriptor carries everything the wave needs, and the (m, l)
+// pairs and accumulators of up to 32 partitions are requested together, so a
+// wave waits for two round trips to memory (descriptor, then partials).
 // ---------------------------------------------------------------------------
 struct MergeParams {
     uint16_t* out;
-    const int32_t* cu;
-    const int32_t* ctx;
     const int32_t* hdr;
-    const int32_t* merge_list;
-    const int32_t* dec_base;
+    const int4* merge_list;
     const float* ws_ml;
     const float* ws_acc;
     int64_t cap_dec;
-    int32_t hq, A;
+    int32_t hq;
 };
 
 template <int A>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
     constexpr int DPL = A >= 64 ? A / 64 : 1;  // dims per lane
+    constexpr int CH = 32;                      // partitions per batch of loads
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    if ((int)blockIdx.x >= P.hdr[HDR_N_MERGE]) return;
     const int h = blockIdx.y * 4 + wave;
-    if (h >= P.hq) return;
-    const int s = P.merge_list[blockIdx.x];
-    const int L = P.ctx[s] + 1;
-    const int np = (L + DECODE_PART - 1) / DECODE_PART;
-    const int64_t base = P.dec_base[s];
+    const int n_merge = P.hdr[HDR_N_MERGE];
+    // The descriptor is requested together with the count (both conditions
+    // are evaluated, so neither load waits for the other); an entry at or
+    // past the count is stale and is never used.
+    const int4 desc = P.merge_list[blockIdx.x];
+    if (((int)blockIdx.x >= n_merge) | (desc.z < 2) | (h >= P.hq)) return;
+    const int64_t base = desc.y;
+    const int np = desc.z;
     if (base < 0 || base + np > P.cap_dec) return;  // never true for a planned sequence
-    const int d0 = lane * DPL;
+    const int d0 = min(lane * DPL, A - DPL);
     float M = NEG_BIG, den = 0.f, num[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) num[i] = 0.f;
-    // Partitions in groups of 64: lane p holds partition p's (m, l); every
-    // lane streams the accumulators of all partitions for its dims.
-    for (int c0 = 0; c0 < np; c0 += 64) {
-        const int n = min(64, np - c0);
-        const int pi = min(lane, n - 1);
-        const float2 ml = *reinterpret_cast<const float2*>(P.ws_ml + ((base + c0 + pi) * P.hq + h) * 2);
-        const float mp = lane < n ? ml.x : NEG_BIG;
-        float cm = mp;
+    for (int c0 = 0; c0 < np; c0 += CH) {
+        const int n = min(CH, np - c0);
+        // lane p < n: (m, l) of partition c0 + p; every lane: its dims of all n
+        float2 ml = make_float2(NEG_BIG, 0.f);
+        if (lane < n)
+            ml = *reinterpret_cast<const float2*>(P.ws_ml + ((base + c0 + lane) * P.hq + h) * 2);
+        const float* accp = P.ws_acc + ((base + c0) * P.hq + h) * A + d0;
+        float acc[CH][DPL];
+#pragma unroll
+        for (int p = 0; p < CH; ++p) {
+            if (p < n) {
+                if constexpr (DPL == 2) {
+                    const float2 v = *reinterpret_cast<const float2*>(accp + (int64_t)p * P.hq * A);
+                    acc[p][0] = v.x;
+                    acc[p][1] = v.y;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < DPL; ++i) acc[p][i] = accp[(int64_t)p * P.hq * A + i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < DPL; ++i) acc[p][i] = 0.f;
+            }
+        }
+        float cm = ml.x;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, shfl_xor_f(cm, off));
         const float Mn = fmaxf(M, cm);
@@ -730,22 +748,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
 #pragma unroll
         for (int i = 0; i < DPL; ++i) num[i] *= a;
         M = Mn;
-        const float w = lane < n ? __builtin_amdgcn_exp2f(mp - M) : 0.f;
-        float wl = lane < n ? w * ml.y : 0.f;
+        const float w = lane < n ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+        float wl = w * ml.y;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) wl += shfl_xor_f(wl, off);
         den += wl;
-        const float* accp = P.ws_acc + ((base + c0) * P.hq + h) * A + min(d0, A - DPL);
-#pragma unroll 8
-        for (int p = 0; p < n; ++p) {
-            const float wp = __shfl(w, p, 64);
 #pragma unroll
-            for (int i = 0; i < DPL; ++i) num[i] = fmaf(wp, accp[(int64_t)p * P.hq * A + i], num[i]);
+        for (int p = 0; p < CH; ++p) {
+            if (p < n) {
+                const float wp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), p));
+#pragma unroll
+                for (int i = 0; i < DPL; ++i) num[i] = fmaf(wp, acc[p][i], num[i]);
+            }
         }
     }
-    if (d0 < A) {
+    if (lane * DPL < A) {
         const float inv = 1.f / den;
-        uint16_t* o = P.out + ((int64_t)P.cu[s] * P.hq + h) * A + d0;
+        uint16_t* o = P.out + ((int64_t)desc.w * P.hq + h) * A + d0;
         if constexpr (DPL == 2) {
             *reinterpret_cast<uint32_t*>(o) = pack_bf16x2(num[0] * inv, num[1] * inv);
         } else {
@@ -796,11 +815,10 @@ hipError_t launch_prep(const StepArgs& a, bool with_append) {
     p.cap_dec = a.lay.cap_dec;
     p.cap_pre = a.lay.cap_pre;
     p.hdr = (int32_t*)(ws + a.lay.hdr);
-    p.dec_base = (int32_t*)(ws + a.lay.dec_base);
     p.dec_items = (int2*)(ws + a.lay.dec_items);
     p.pre_items = (int2*)(ws + a.lay.pre_items);
     p.pre_sorted = (int2*)(ws + a.lay.pre_sorted);
-    p.merge_list = (int32_t*)(ws + a.lay.merge_list);
+    p.merge_list = (int4*)(ws + a.lay.merge_list);
     p.k_new = with_append ? (const uint4*)a.k_new : nullptr;
     p.v_new = with_append ? (const uint4*)a.v_new : nullptr;
     p.k_cache = (uint4*)a.k_cache;
@@ -862,16 +880,12 @@ hipError_t launch_merge(const StepArgs& a) {
     char* ws = a.ws;
     MergeParams mp;
     mp.out = (uint16_t*)a.out;
-    mp.cu = a.cu_seqlens_q;
-    mp.ctx = a.context_lens;
     mp.hdr = (const int32_t*)(ws + a.lay.hdr);
-    mp.merge_list = (const int32_t*)(ws + a.lay.merge_list);
-    mp.dec_base = (const int32_t*)(ws + a.lay.dec_base);
+    mp.merge_list = (const int4*)(ws + a.lay.merge_list);
     mp.ws_ml = (const float*)(ws + a.lay.ml);
     mp.ws_acc = (const float*)(ws + a.lay.acc);
     mp.cap_dec = a.lay.cap_dec;
     mp.hq = a.num_q_heads;
-    mp.A = a.head_dim;
     dim3 mgrid((unsigned)a.num_seqs, (unsigned)((a.num_q_heads + 3) / 4));
     if (a.head_dim == 128)
         hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, a.stream, mp);

@@ -35,7 +35,7 @@ constexpr int PREFILL_QW = 32;
 constexpr int PREFILL_TK = 64;  // keys per LDS tile
 
 struct WsLayout {
-    size_t hdr, dec_base, dec_items, pre_items, pre_sorted, merge_list, ml, acc, total;
+    size_t hdr, dec_items, pre_items, pre_sorted, merge_list, ml, acc, total;
     int64_t cap_dec, cap_pre;
 };
 
@@ -54,11 +54,10 @@ inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context
     w.cap_pre = (int64_t)total_q / prefill_span(G) + num_seqs;
     size_t off = 0;
     w.hdr = off;        off = align_up(off + HDR_WORDS * 4, 256);
-    w.dec_base = off;   off = align_up(off + (size_t)num_seqs * 4, 256);
     w.dec_items = off;  off = align_up(off + (size_t)w.cap_dec * 8, 256);
     w.pre_items = off;  off = align_up(off + (size_t)w.cap_pre * 8, 256);
     w.pre_sorted = off; off = align_up(off + (size_t)w.cap_pre * 8, 256);
-    w.merge_list = off; off = align_up(off + (size_t)num_seqs * 4, 256);
+    w.merge_list = off; off = align_up(off + (size_t)num_seqs * 16, 256);
     w.ml = off;         off = align_up(off + (size_t)w.cap_dec * num_q_heads * 2 * 4, 256);
     w.acc = off;        off = align_up(off + (size_t)w.cap_dec * num_q_heads * head_dim * 4, 256);
     w.total = off;

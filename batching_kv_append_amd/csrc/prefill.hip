@@ -42,6 +42,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct PrefillParams {
     const uint16_t* q;
@@ -149,15 +150,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
     // keys a lane feeds to one P.V step (16a+4c+{0..3} and 16a+8+4c+{0..3})
     // form one 16-byte chunk (2a+c) of the transposed row.
     const int vunit = 4 * (kg >> 2) + 2 * (kg & 1) + ((kg >> 1) & 1);
-    uint4 kreg[4], vreg[4];
+    u32x4_t kreg[4], vreg[4];  // native vectors: the staging stays in VGPRs
     int bad = 0;
-    auto load_tile = [&](int k0) {
+    // Block-table entry of this thread's key group in the tile at k0 (-1 past
+    // the table).  Read one tile ahead of its use, so the K/V addresses never
+    // wait for the table.
+    auto table_entry = [&](int k0) __attribute__((always_inline)) -> int {
+        const int lb = min(k0 + 4 * kg, L - 1) / BS;
+        return lb < P.max_blocks ? P.table[(int64_t)s * P.max_blocks + lb] : -1;
+    };
+    auto load_tile = [&](int k0, int entry) __attribute__((always_inline)) {
         if (!loader) return;
-        const int key0 = min(k0 + 4 * kg, L - 1);
-        const int lb = key0 / BS;  // the (clamped) 4 keys share one block
-        int64_t blk = 0;
-        if (lb < P.max_blocks) blk = P.table[(int64_t)s * P.max_blocks + lb];
-        if (lb >= P.max_blocks || blk < 0 || blk >= P.num_blocks) {
+        const int key0 = min(k0 + 4 * kg, L - 1);  // the (clamped) 4 keys share one block
+        int64_t blk = entry;
+        if (blk < 0 || blk >= P.num_blocks) {
             bad = 1;
             blk = 0;
         }
@@ -167,29 +173,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
         if (k0 + 4 * kg + 3 < L) {  // whole group in range: constant row offsets
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                kreg[j] = kp[j * CPR];
-                vreg[j] = vp[j * CPR];
+                kreg[j] = __builtin_bit_cast(u32x4_t, kp[j * CPR]);
+                vreg[j] = __builtin_bit_cast(u32x4_t, vp[j * CPR]);
             }
         } else {  // the sequence's last keys: rows past L repeat row L-1
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int dj = min(k0 + 4 * kg + j, L - 1) - key0;
-                kreg[j] = kp[dj * CPR];
-                vreg[j] = vp[dj * CPR];
+                kreg[j] = __builtin_bit_cast(u32x4_t, kp[dj * CPR]);
+                vreg[j] = __builtin_bit_cast(u32x4_t, vp[dj * CPR]);
             }
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
         if (!loader) return;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = 4 * kg + j;
-            sK[buf][key * CPR + (cc ^ (key % CPR))] = kreg[j];
+            sK[buf][key * CPR + (cc ^ (key % CPR))] = __builtin_bit_cast(uint4, kreg[j]);
         }
-        const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-        const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-        const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-        const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+        const u32x4_t w0 = vreg[0], w1 = vreg[1], w2 = vreg[2], w3 = vreg[3];
         uint2* vt = reinterpret_cast<uint2*>(&sVt[buf][0]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -208,15 +211,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
         }
     };
 
+    int entry_next = 0;  // table entry of the tile after the one being loaded
     if (nkt > 0) {
-        load_tile(0);
+        load_tile(0, table_entry(0));
+        if (nkt > 1) entry_next = table_entry(TK);
         store_tile(0);
     }
     __syncthreads();
+    // Explicit wait for everything issued so far (the Q^T operand loads are
+    // conditional, and without it the compiler assumes they may still be in
+    // flight inside the loop and waits for ALL loads, the next tile's
+    // included, before the first MFMA of every tile).
+    __builtin_amdgcn_s_waitcnt(0);
     for (int t = 0; t < nkt; ++t) {
         const int k0 = t * TK;
         const int buf = t & 1;
-        if (t + 1 < nkt) load_tile(k0 + TK);  // in flight during this tile's math
+        if (t + 1 < nkt) {  // in flight during this tile's math
+            const int entry = entry_next;
+            if (t + 2 < nkt) entry_next = table_entry(k0 + 2 * TK);
+            load_tile(k0 + TK, entry);
+        }
 
         if (k0 < kend_w) {
             // Raised wave priority around the two MFMA blocks: a wave that

@@ -73,6 +73,13 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 with (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
 // XOR swizzle of the 16-byte chunks of V^T row d.  Reads: 8 (or 16)
 // consecutive rows d at one logical chunk hit distinct bank groups.  Writes:
 // rows d = 8*cc + e of one e over cc = 0..7 hit distinct chunks.
@@ -144,8 +151,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
     // same block): their weight is exactly 0 for every row that is stored,
     // and the copy keeps their values finite.
     const bool loader = tid < LOADERS;
-    const int kg = tid / CPR;  // key group: keys 4kg .. 4kg+3 of the tile
-    const int cc = tid % CPR;  // 16-byte chunk of the row (dims 8cc .. 8cc+7)
+    // Thread -> (key group kg: keys 4kg .. 4kg+3, 16-byte chunk cc: dims
+    // 8cc .. 8cc+7).  Wave w covers key groups 4w .. 4w+3.  For A = 128 each
+    // 16-lane group holds chunks 8h .. 8h+7 of key groups kg and kg ^ 2, so
+    // its eight-byte V^T stores land on 16 distinct bank pairs (kg and kg ^ 2
+    // write opposite halves of a 16-byte unit).
+    int kg, cc;
+    if constexpr (CPR == 16) {
+        kg = ((tid >> 5) & 1) | (((tid >> 3) & 1) << 1) | ((tid >> 6) << 2);
+        cc = (tid & 7) | (((tid >> 4) & 1) << 3);
+    } else {
+        kg = tid / CPR;
+        cc = tid % CPR;
+    }
     // V^T key order: key 16a+8b+4c+e is stored at 16a+8c+4b+e, so the eight
     // keys a lane feeds to one P.V step (16a+4c+{0..3} and 16a+8+4c+{0..3})
     // form one 16-byte chunk (2a+c) of the transposed row.
@@ -298,16 +316,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
             for (int kh = 0; kh < 2; ++kh) {
                 float p[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][r], mc, -m));
-                    lsum += p[r];
-                }
+                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][r], mc, -m));
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     pb[kh][ks].x = pack_bf16x2(p[ks * 8 + 0], p[ks * 8 + 1]);
                     pb[kh][ks].y = pack_bf16x2(p[ks * 8 + 2], p[ks * 8 + 3]);
                     pb[kh][ks].z = pack_bf16x2(p[ks * 8 + 4], p[ks * 8 + 5]);
                     pb[kh][ks].w = pack_bf16x2(p[ks * 8 + 6], p[ks * 8 + 7]);
+                    // the denominator sums the same bf16 weights the P.V
+                    // product uses: one dot2 with (1, 1) per pair
+                    lsum = sum_bf16x2(pb[kh][ks].x, lsum);
+                    lsum = sum_bf16x2(pb[kh][ks].y, lsum);
+                    lsum = sum_bf16x2(pb[kh][ks].z, lsum);
+                    lsum = sum_bf16x2(pb[kh][ks].w, lsum);
                 }
             }
 

@@ -2,9 +2,11 @@
 
 ``python batching_kv_append_amd/build.py`` compiles every source under
 ``csrc/`` to an object in ``_build/`` and links ``libkvc.so`` next to this
-file.  All HIP code is compiled with packed-fp32 instructions disabled
-(``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns
-that it does not know that feature, which is harmless.
+file, plus ``libkvc_probe.so`` (streaming-read kernels the benchmark uses to
+measure the practical HBM read ceiling; not part of the library's ABI).  All
+HIP code is compiled with packed-fp32 instructions disabled (``-Xclang
+-target-feature -Xclang -packed-fp32-ops``); the host pass warns that it does
+not know that feature, which is harmless.
 """
 from __future__ import annotations
 
@@ -19,10 +21,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvc.so")
+PROBE_LIB = os.path.join(HERE, "libkvc_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["status.cpp", "allocator.cpp", "api.hip", "cache_ops.hip", "decode.hip", "prefill.hip"]
+PROBE_SOURCES = ["stream_probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
           f"-I{INCLUDE}", f"-I{CSRC}"]
@@ -49,18 +53,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile and link libkvc.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(8, os.cpu_count() or 1)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile and link libkvc.so (and libkvc_probe.so); returns libkvc.so's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

@@ -1,0 +1,94 @@
+// Measurement helper, not part of the attention library's ABI: plain
+// streaming-read kernels that give the practical HBM read ceiling the decode
+// kernel is compared with (beside the 8 TB/s data-sheet figure).  Built into
+// its own shared library (libkvc_probe.so) and used only by the benchmark.
+//
+//   kvcp_seq_read    every byte of a buffer once, 16 bytes per lane, grid-stride
+//   kvcp_block_read  whole 4 KiB blocks in the order of a permutation, one wave
+//                    per block group: the decode kernel's access pattern (one kv
+//                    head of a 16-token block of 128 bf16 dims is 4 KiB)
+//
+// Both reduce what they read into one word per thread so that the loads are
+// not removed; `out` needs grid * 256 uint32 words.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+template <int U>
+__global__ __launch_bounds__(256) void seq_read(const uint4* __restrict__ p, int64_t n16,
+                                                uint32_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    uint32_t acc = 0;
+    for (int64_t base = (int64_t)blockIdx.x * 256 + threadIdx.x; base < n16; base += stride * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t i = base + k * stride;
+            v[k] = i < n16 ? p[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// Wave w reads blocks perm[w*U .. w*U+U-1], then skips ahead by all waves.
+template <int U>
+__global__ __launch_bounds__(256) void block_read(const uint4* __restrict__ p,
+                                                  const int32_t* __restrict__ perm, int64_t nblk,
+                                                  uint32_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    uint32_t acc = 0;
+    for (int64_t b0 = w * U; b0 < nblk; b0 += nw * U) {
+        uint4 v[U][4];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t b = b0 + k;
+            const int64_t pb = b < nblk ? perm[b] : 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[k][j] = b < nblk ? p[pb * 256 + j * 64 + lane] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc ^= v[k][j].x ^ v[k][j].y ^ v[k][j].z ^ v[k][j].w;
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+// n16: buffer size in 16-byte units; unroll in {4, 8, 16}.  Returns a hipError_t.
+extern "C" int kvcp_seq_read(const void* p, int64_t n16, void* out, int grid, int unroll,
+                             void* stream) {
+    if (!p || !out || n16 < 0 || grid < 1) return (int)hipErrorInvalidValue;
+    hipStream_t st = (hipStream_t)stream;
+    switch (unroll) {
+        case 4: hipLaunchKernelGGL(seq_read<4>, dim3(grid), dim3(256), 0, st, (const uint4*)p, n16, (uint32_t*)out); break;
+        case 8: hipLaunchKernelGGL(seq_read<8>, dim3(grid), dim3(256), 0, st, (const uint4*)p, n16, (uint32_t*)out); break;
+        case 16: hipLaunchKernelGGL(seq_read<16>, dim3(grid), dim3(256), 0, st, (const uint4*)p, n16, (uint32_t*)out); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+// p holds nblk 4 KiB blocks; perm is a permutation of 0 .. nblk-1 (device,
+// int32); unroll in {2, 4, 8}.  Returns a hipError_t.
+extern "C" int kvcp_block_read(const void* p, const void* perm, int64_t nblk, void* out, int grid,
+                               int unroll, void* stream) {
+    if (!p || !perm || !out || nblk < 0 || grid < 1) return (int)hipErrorInvalidValue;
+    hipStream_t st = (hipStream_t)stream;
+    const uint4* b = (const uint4*)p;
+    const int32_t* pm = (const int32_t*)perm;
+    switch (unroll) {
+        case 2: hipLaunchKernelGGL(block_read<2>, dim3(grid), dim3(256), 0, st, b, pm, nblk, (uint32_t*)out); break;
+        case 4: hipLaunchKernelGGL(block_read<4>, dim3(grid), dim3(256), 0, st, b, pm, nblk, (uint32_t*)out); break;
+        case 8: hipLaunchKernelGGL(block_read<8>, dim3(grid), dim3(256), 0, st, b, pm, nblk, (uint32_t*)out); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}

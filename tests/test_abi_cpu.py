@@ -35,6 +35,14 @@ def test_library_exports_every_declared_symbol(kvc):
     assert sorted(kvc.EXPORTED) == declared_functions()
 
 
+def test_measurement_probe_library_loads():
+    # streaming-read kernels the benchmark uses for the practical read ceiling
+    path = os.path.join(ROOT, "batching_kv_append_amd", "libkvc_probe.so")
+    assert os.path.exists(path), "build with batching_kv_append_amd/build.py"
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "kvcp_seq_read") and hasattr(lib, "kvcp_block_read")
+
+
 def test_status_strings(kvc):
     for code in [0, -1, -2, -3, -4, -5]:
         assert kvc.kvc_status_string(code) not in ("", "unknown status")

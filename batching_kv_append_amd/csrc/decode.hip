@@ -59,9 +59,21 @@ struct PrepParams {
     int32_t max_blocks, hkv, head_dim, block_size;
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
 // Workgroup 0 plans; workgroups 1.. append the new rows (one wave per row).
-// Only the planner writes the flag word (it zeroes it first): it also checks
-// the table entries the append will use, and the append skips bad entries.
+// Only the planner writes the flag word (it zeroes it first).  The append
+// skips a row whose block is outside the table or the pool; every appended
+// position is read by the attention kernels (a row always sees its own key),
+// which report such blocks (TABLE_SHORT / BAD_BLOCK) when they read them.
 __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     if (blockIdx.x > 0) {
         const int64_t t = (int64_t)(blockIdx.x - 1) * (PLAN_THREADS / 64) + (threadIdx.x >> 6);
@@ -70,6 +82,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
                    P.cu, P.ctx, P.num_seqs, t, P.hkv, P.head_dim, P.block_size, threadIdx.x & 63);
         return;
     }
+    constexpr int WAVES = PLAN_THREADS / 64;
     const int32_t* __restrict__ cu = P.cu;
     const int32_t* __restrict__ ctx = P.ctx;
     const int32_t num_seqs = P.num_seqs, total_q = P.total_q, max_q_len = P.max_q_len;
@@ -80,25 +93,27 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     int2* pre_items = P.pre_items;
     int2* pre_sorted = P.pre_sorted;
     int4* merge_list = P.merge_list;
-    __shared__ int sc[3][PLAN_THREADS];
+    __shared__ int wsum[3][WAVES];
     __shared__ int hist[COST_BUCKETS];
     __shared__ int carry[3];
     __shared__ int flags;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     if (tid == 0) {
         carry[0] = carry[1] = carry[2] = 0;
         flags = 0;
         hdr[HDR_FLAGS] = 0;
     }
+    for (int b = tid; b < COST_BUCKETS; b += PLAN_THREADS) hist[b] = 0;
     __syncthreads();
     for (int base = 0; base < num_seqs; base += PLAN_THREADS) {
         const int s = base + tid;
-        int nd = 0, np = 0, nm = 0, q = 0, row0 = 0;
+        int nd = 0, np = 0, nm = 0, row0 = 0;
         if (s < num_seqs) {
             const int r0 = cu[s], r1 = cu[s + 1];
-            row0 = r0;
             const int c = ctx[s];
-            q = r1 - r0;
+            int q = r1 - r0;
+            row0 = r0;
             // A sequence whose rows are not inside [0, total_q) or whose
             // lengths break the host bounds is skipped (and flagged): no
             // later kernel touches its rows, so garbage lengths can never
@@ -116,38 +131,21 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
             } else if (q >= 2) {
                 np = (q + span - 1) / span;
             }
-            if (P.k_new != nullptr && r1 > r0 && r0 >= 0 && r1 <= total_q && c >= 0) {
-                // blocks holding positions c .. c + (r1 - r0) - 1 (the append's targets)
-                const int64_t lb_lo = c / P.block_size;
-                const int64_t lb_hi = ((int64_t)c + (r1 - r0) - 1) / P.block_size;
-                for (int64_t lb = lb_lo; lb <= lb_hi; ++lb) {
-                    if (lb >= P.max_blocks) { atomicOr(&flags, FLAG_TABLE_SHORT); break; }
-                    const int32_t id = P.table[(int64_t)s * P.max_blocks + lb];
-                    if (id < 0 || id >= P.num_blocks) atomicOr(&flags, FLAG_BAD_BLOCK);
-                }
-            }
         }
-        sc[0][tid] = nd;
-        sc[1][tid] = np;
-        sc[2][tid] = nm;
+        // exclusive offsets: scan inside the wave, then the wave totals
+        const int id = wave_scan(nd, lane), ip = wave_scan(np, lane), im = wave_scan(nm, lane);
+        if (lane == 63) {
+            wsum[0][wave] = id;
+            wsum[1][wave] = ip;
+            wsum[2][wave] = im;
+        }
         __syncthreads();
-        // inclusive Hillis-Steele scan of the three counts
-        for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-            int a0 = 0, a1 = 0, a2 = 0;
-            if (tid >= off) {
-                a0 = sc[0][tid - off];
-                a1 = sc[1][tid - off];
-                a2 = sc[2][tid - off];
-            }
-            __syncthreads();
-            sc[0][tid] += a0;
-            sc[1][tid] += a1;
-            sc[2][tid] += a2;
-            __syncthreads();
+        int od = carry[0] + id - nd, op = carry[1] + ip - np, om = carry[2] + im - nm;
+        for (int w = 0; w < wave; ++w) {
+            od += wsum[0][w];
+            op += wsum[1][w];
+            om += wsum[2][w];
         }
-        const int od = carry[0] + sc[0][tid] - nd;
-        const int op = carry[1] + sc[1][tid] - np;
-        const int om = carry[2] + sc[2][tid] - nm;
         if (s < num_seqs) {
             for (int j = 0; j < nd; ++j) {
                 if (od + j < cap_dec) dec_items[od + j] = make_int2(s, j);
@@ -160,11 +158,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
             }
             if (nm) merge_list[om] = make_int4(s, od, nd, row0);
         }
-        __syncthreads();
-        if (tid == PLAN_THREADS - 1) {
-            carry[0] += sc[0][tid];
-            carry[1] += sc[1][tid];
-            carry[2] += sc[2][tid];
+        __syncthreads();  // every thread has read carry and wsum
+        if (tid < 3) {
+            int t = 0;
+            for (int w = 0; w < WAVES; ++w) t += wsum[tid][w];
+            carry[tid] += t;
         }
         __syncthreads();
     }
@@ -172,8 +170,6 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     // 64-key tiles a workgroup walks), so the longest workgroups start first
     // and the short ones fill the tail.
     const int npre = (int)min((int64_t)carry[1], cap_pre);
-    for (int b = tid; b < COST_BUCKETS; b += PLAN_THREADS) hist[b] = 0;
-    __syncthreads();
     auto bucket_of = [&](int2 item) {
         const int q = cu[item.x + 1] - cu[item.x];
         const int64_t keys = (int64_t)ctx[item.x] + min((item.y + 1) * span, q);
@@ -183,16 +179,14 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     for (int i = tid; i < npre; i += PLAN_THREADS) atomicAdd(&hist[bucket_of(pre_items[i])], 1);
     __syncthreads();
     {  // exclusive scan of the histogram (one bucket per thread)
-        const int v = tid < COST_BUCKETS ? hist[tid] : 0;
-        sc[0][tid] = v;
+        static_assert(COST_BUCKETS == PLAN_THREADS, "one bucket per thread");
+        const int v = hist[tid];
+        const int iv = wave_scan(v, lane);
+        if (lane == 63) wsum[0][wave] = iv;
         __syncthreads();
-        for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-            const int a0 = tid >= off ? sc[0][tid - off] : 0;
-            __syncthreads();
-            sc[0][tid] += a0;
-            __syncthreads();
-        }
-        if (tid < COST_BUCKETS) hist[tid] = sc[0][tid] - v;
+        int o = iv - v;
+        for (int w = 0; w < wave; ++w) o += wsum[0][w];
+        hist[tid] = o;
     }
     __syncthreads();
     for (int i = tid; i < npre; i += PLAN_THREADS) {
@@ -267,10 +261,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
         // table slice of this partition: lane i holds entry (t0 / BS + i)
         const int lb0 = t0 / BS;
         const int nlb = (t1 - t0 + BS - 1) / BS;
-        int tbl = -1;
+        int tbl = -1, short_tbl = 0;  // short_tbl: a needed block is past the table row
         if (lane < nlb && lane < NT) {
             const int64_t lb = lb0 + lane;
             if (lb < P.max_blocks) tbl = P.table[(int64_t)s * P.max_blocks + lb];
+            else short_tbl = 1;
         }
 
         // q for GW heads, pre-scaled into the exp2 domain
@@ -369,7 +364,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
                 }
             }
         }
-        if (bad && lane == 0) set_flag(P.hdr, FLAG_BAD_BLOCK);
+        // a block past the table reads as id -1: reported as a short table
+        if (__any(short_tbl)) {
+            if (lane == 0) set_flag(P.hdr, FLAG_TABLE_SHORT);
+        } else if (__any(bad)) {
+            if (lane == 0) set_flag(P.hdr, FLAG_BAD_BLOCK);
+        }
 
         // merge the RPL row groups of the wave (lanes c8, c8+LPR, ...)
 #pragma unroll
@@ -493,10 +493,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     // table slice: lane i holds entry (t0 / BS + i)
     const int lb0 = t0 / BS;
     const int nlb = (t1 - t0 + BS - 1) / BS;
-    int tbl = -1;
+    int tbl = -1, short_tbl = 0;  // short_tbl: a needed block is past the table row
     if (lane < nlb && lane < NT) {
         const int64_t lb = lb0 + lane;
         if (lb < P.max_blocks) tbl = P.table[(int64_t)s * P.max_blocks + lb];
+        else short_tbl = 1;
     }
 
     // Q^T operand: column col = head h0+col (zero past GW), dims 32ks + 8g .. +7
@@ -646,7 +647,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
             o[dt] = mfma16(a, pb, o[dt]);
         }
     }
-    if (bad && lane == 0) set_flag(P.hdr, FLAG_BAD_BLOCK);
+    // a block past the table reads as id -1: reported as a short table
+    if (__any(short_tbl)) {
+        if (lane == 0) set_flag(P.hdr, FLAG_TABLE_SHORT);
+    } else if (__any(bad)) {
+        if (lane == 0) set_flag(P.hdr, FLAG_BAD_BLOCK);
+    }
 
     // ---- column totals and output ----------------------------------------------
     float lt = lsum + __shfl_xor(lsum, 16, 64);

@@ -173,9 +173,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
     // Block-table entry of this thread's key group in the tile at k0 (-1 past
     // the table).  Read one tile ahead of its use, so the K/V addresses never
     // wait for the table.
+    int short_tbl = 0;  // a needed block is past the table row
     auto table_entry = [&](int k0) __attribute__((always_inline)) -> int {
         const int lb = min(k0 + 4 * kg, L - 1) / BS;
-        return lb < P.max_blocks ? P.table[(int64_t)s * P.max_blocks + lb] : -1;
+        if (lb < P.max_blocks) return P.table[(int64_t)s * P.max_blocks + lb];
+        short_tbl = 1;
+        return 0;  // in range; the result is flagged
     };
     auto load_tile = [&](int k0, int entry) __attribute__((always_inline)) {
         if (!loader) return;
@@ -353,6 +356,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
         if (t + 1 < nkt) store_tile(buf ^ 1);
         __syncthreads();
     }
+    if (short_tbl) atomicOr(P.hdr + HDR_FLAGS, FLAG_TABLE_SHORT);
     if (bad) atomicOr(P.hdr + HDR_FLAGS, FLAG_BAD_BLOCK);
 
     // ---- normalise and store ------------------------------------------------

@@ -56,8 +56,31 @@ struct PrefillParams {
     const int2* items;
     int64_t num_blocks;
     int32_t max_blocks, hq, hkv, G, HC;
+    int32_t xcd_map;   // 1: head slots % 8 == 0, 2: 8 % head slots == 0, 0: plain
     float scale_log2;  // scale * log2(e)
 };
+
+// Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
+// linear id.  The grid is one-dimensional over (work item, head slot), head
+// slot = kv head x head chunk, laid out so that one XCD serves a fixed set of
+// head slots: the K/V of a kv head are then fetched into one L2 (or, with
+// fewer than 8 slots, into 8 / slots of them) instead of all eight.  Within
+// an XCD, items keep the planner's costliest-first order.
+__device__ __forceinline__ void prefill_unit(int L, int slots, int mode, int& item, int& slot) {
+    const int xcd = L & 7, r = L >> 3;
+    if (mode == 1) {
+        const int per = slots >> 3;
+        slot = (r % per) * 8 + xcd;
+        item = r / per;
+    } else if (mode == 2) {
+        const int groups = 8 / slots;
+        slot = xcd % slots;
+        item = r * groups + xcd / slots;
+    } else {
+        slot = L % slots;
+        item = L / slots;
+    }
+}
 
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -108,11 +131,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
     const int hi = lane >> 5;   // which half of the wave
     const int col = lane & 31;  // query column of this lane
 
-    if ((int)blockIdx.x >= P.hdr[HDR_N_PRE]) return;
-    const int2 it = P.items[blockIdx.x];
+    int item, slot;
+    prefill_unit((int)blockIdx.x, P.hkv * P.HC, P.xcd_map, item, slot);
+    if (item >= P.hdr[HDR_N_PRE]) return;
+    const int2 it = P.items[item];
     const int s = it.x, tile = it.y;
-    const int kvh = blockIdx.y / P.HC;
-    const int hc = blockIdx.y % P.HC;
+    const int kvh = slot / P.HC;
+    const int hc = slot % P.HC;
     const int h = kvh * P.G + hc * HPW + (wave % HPW);
     const int row0 = P.cu[s];
     const int qlen = P.cu[s + 1] - row0;
@@ -413,10 +438,12 @@ hipError_t launch_prefill(const StepArgs& a) {
     p.G = G;
     p.HC = G / hpw;
     p.scale_log2 = a.scale * 1.4426950408889634f;
-    const int64_t gx = a.lay.cap_pre;
+    const int slots = a.num_kv_heads * p.HC;
+    p.xcd_map = (slots % 8 == 0) ? 1 : (8 % slots == 0) ? 2 : 0;
+    const int64_t gx = a.lay.cap_pre * slots;
     if (gx <= 0) return hipSuccess;
     if (gx > INT32_MAX) return hipErrorInvalidValue;
-    dim3 grid((unsigned)gx, (unsigned)(a.num_kv_heads * p.HC));
+    dim3 grid((unsigned)gx);
     if (a.head_dim == 128) {
         if (a.block_size == 16) launch_prefill_hpw<128, 16>(a, p, hpw, grid);
         else launch_prefill_hpw<128, 4>(a, p, hpw, grid);

@@ -453,7 +453,10 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.hi | b.hi << 16
 }
 
-template <int BS>
+// NG: 16-column groups of q heads per wave (1, or 2 for 32 heads on one kv
+// head, as in MQA): the groups share every K fragment and the V^T tile, so
+// the partition's K/V is read once for all of them.
+template <int BS, int NG>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     constexpr int A = 128;
     constexpr int CPR = A / 8;              // 16-byte chunks per row
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     if (u >= n_units) return;
     uint4* vt = &sVt[wave][0];
 
-    const int GW = P.G / P.HC;  // heads of this wave (<= 16)
+    const int GW = P.G / P.HC;  // heads of this wave (<= 16 * NG)
     const int hc = u % P.HC;
     const int kvh = (u / P.HC) % P.hkv;
     const int item = u / (P.HC * P.hkv);
@@ -500,20 +503,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
         else short_tbl = 1;
     }
 
-    // Q^T operand: column col = head h0+col (zero past GW), dims 32ks + 8g .. +7
-    uint4 qb[4];
+    // Q^T operand of group ng: column col = head h0 + 16ng + col (zero past
+    // GW), dims 32ks + 8g .. +7
+    uint4 qb[NG][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        qb[ks] = make_uint4(0, 0, 0, 0);
-        if (col < GW)
-            qb[ks] = *reinterpret_cast<const uint4*>(
-                P.q + (((int64_t)row * P.hq + h0 + col) * A + ks * 32 + g * 8));
-    }
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            qb[ng][ks] = make_uint4(0, 0, 0, 0);
+            if (16 * ng + col < GW)
+                qb[ng][ks] = *reinterpret_cast<const uint4*>(
+                    P.q + (((int64_t)row * P.hq + h0 + 16 * ng + col) * A + ks * 32 + g * 8));
+        }
 
-    f32x4_t o[8];  // O^T rows 16dt + 4g + r, column col
+    f32x4_t o[NG][8];  // O^T rows 16dt + 4g + r, column col of group ng
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = -1.0e30f, lsum = 0.f;
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[ng][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m[NG], lsum[NG];
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng) {
+        m[ng] = -1.0e30f;
+        lsum[ng] = 0.f;
+    }
     int bad = 0;
 
     // Block id of token t (< t1) through the table slice.  With 16-token
@@ -560,14 +573,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
             }
         }
 
-        // ---- S^T for the two blocks ------------------------------------------
-        f32x4_t sc[2];
+        // ---- S^T for the two blocks, per head group ---------------------------
+        f32x4_t sc[NG][2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            sc[b] = mfma16(kb[b][0], qb[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-            for (int ks = 1; ks < 4; ++ks) sc[b] = mfma16(kb[b][ks], qb[ks], sc[b]);
-        }
+            for (int b = 0; b < 2; ++b) {
+                sc[ng][b] = mfma16(kb[b][0], qb[ng][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int ks = 1; ks < 4; ++ks) sc[ng][b] = mfma16(kb[b][ks], qb[ng][ks], sc[ng][b]);
+            }
 
         // ---- V^T into LDS (this wave's tile): 8-byte units of 4 tokens ------
         // The 4x8 transpose is written as vector interleaves of whole rows
@@ -593,58 +608,62 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
             }
         }
 
-        // ---- online softmax of this lane's column ----------------------------
+        // ---- online softmax of this lane's column, per head group ------------
         const bool tail = tc + STEP > t1;
-        float v8[8];
+        const float mc = pos_scale ? cs : 1.f;
+        uint4 pb[NG];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            v8[r] = sc[0][r];
-            v8[4 + r] = sc[1][r];
-        }
-        if (!pos_scale) {
+        for (int ng = 0; ng < NG; ++ng) {
+            float v8[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) v8[r] *= cs;
-        }
-        if (tail) {
+            for (int r = 0; r < 4; ++r) {
+                v8[r] = sc[ng][0][r];
+                v8[4 + r] = sc[ng][1][r];
+            }
+            if (!pos_scale) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) v8[r] *= cs;
+            }
+            if (tail) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int t = tc + (r >> 2) * 16 + 4 * g + (r & 3);
+                    if (t >= t1) v8[r] = -INFINITY;
+                }
+            }
+            float mx = fmaxf(fmaxf(fmaxf(v8[0], v8[1]), fmaxf(v8[2], v8[3])),
+                             fmaxf(fmaxf(v8[4], v8[5]), fmaxf(v8[6], v8[7])));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float cand = pos_scale ? mx * cs : mx;
+            const bool grow = cand > m[ng] + RESCALE_SLACK;
+            if (__any(grow)) {
+                const float m_new = grow ? cand : m[ng];
+                const float alpha = __builtin_amdgcn_exp2f(m[ng] - m_new);
+                m[ng] = m_new;
+                lsum[ng] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[ng][dt] *= alpha;
+            }
+            float p[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const int t = tc + (r >> 2) * 16 + 4 * g + (r & 3);
-                if (t >= t1) v8[r] = -INFINITY;
+                p[r] = __builtin_amdgcn_exp2f(fmaf(v8[r], mc, -m[ng]));
+                lsum[ng] += p[r];
             }
+            pb[ng].x = pack_bf16x2(p[0], p[1]);
+            pb[ng].y = pack_bf16x2(p[2], p[3]);
+            pb[ng].z = pack_bf16x2(p[4], p[5]);
+            pb[ng].w = pack_bf16x2(p[6], p[7]);
         }
-        float mx = fmaxf(fmaxf(fmaxf(v8[0], v8[1]), fmaxf(v8[2], v8[3])),
-                         fmaxf(fmaxf(v8[4], v8[5]), fmaxf(v8[6], v8[7])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float cand = pos_scale ? mx * cs : mx;
-        const bool grow = cand > m + RESCALE_SLACK;
-        if (__any(grow)) {
-            const float m_new = grow ? cand : m;
-            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-            m = m_new;
-            lsum *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-        }
-        const float mc = pos_scale ? cs : 1.f;
-        float p[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(fmaf(v8[r], mc, -m));
-            lsum += p[r];
-        }
-        uint4 pb;
-        pb.x = pack_bf16x2(p[0], p[1]);
-        pb.y = pack_bf16x2(p[2], p[3]);
-        pb.z = pack_bf16x2(p[4], p[5]);
-        pb.w = pack_bf16x2(p[6], p[7]);
 
-        // ---- O^T += V^T P^T ------------------------------------------------------
+        // ---- O^T += V^T P^T (one V^T fragment for all head groups) ------------
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const int d = dt * 16 + col;
             const uint4 a = vt[d * 4 + (g ^ ((d >> 2) & 3))];
-            o[dt] = mfma16(a, pb, o[dt]);
+#pragma unroll
+            for (int ng = 0; ng < NG; ++ng) o[ng][dt] = mfma16(a, pb[ng], o[ng][dt]);
         }
     }
     // a block past the table reads as id -1: reported as a short table
@@ -655,30 +674,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     }
 
     // ---- column totals and output ----------------------------------------------
-    float lt = lsum + __shfl_xor(lsum, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    if (col < GW) {
-        const int h = h0 + col;
-        if (nparts == 1) {
-            const float inv = 1.f / lt;
-            uint16_t* orow = P.out + ((int64_t)row * P.hq + h) * A;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                uint2 v;
-                v.x = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-                v.y = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-                *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * g) = v;
-            }
-        } else {
-            const int64_t slot = (int64_t)item * P.hq + h;
-            float* acc = P.ws_acc + slot * A;
+    for (int ng = 0; ng < NG; ++ng) {
+        float lt = lsum[ng] + __shfl_xor(lsum[ng], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        if (16 * ng + col < GW) {
+            const int h = h0 + 16 * ng + col;
+            if (nparts == 1) {
+                const float inv = 1.f / lt;
+                uint16_t* orow = P.out + ((int64_t)row * P.hq + h) * A;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                *reinterpret_cast<float4*>(acc + dt * 16 + 4 * g) =
-                    make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-            if (g == 0) {
-                P.ws_ml[slot * 2] = m;
-                P.ws_ml[slot * 2 + 1] = lt;
+                for (int dt = 0; dt < 8; ++dt) {
+                    uint2 v;
+                    v.x = pack_bf16x2(o[ng][dt][0] * inv, o[ng][dt][1] * inv);
+                    v.y = pack_bf16x2(o[ng][dt][2] * inv, o[ng][dt][3] * inv);
+                    *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * g) = v;
+                }
+            } else {
+                const int64_t slot = (int64_t)item * P.hq + h;
+                float* acc = P.ws_acc + slot * A;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+                    *reinterpret_cast<float4*>(acc + dt * 16 + 4 * g) =
+                        make_float4(o[ng][dt][0], o[ng][dt][1], o[ng][dt][2], o[ng][dt][3]);
+                if (g == 0) {
+                    P.ws_ml[slot * 2] = m[ng];
+                    P.ws_ml[slot * 2 + 1] = lt;
+                }
             }
         }
     }
@@ -799,7 +821,8 @@ void launch_decode_gw(const StepArgs& a, const DecodeParams& p, int GW, int grid
 }  // namespace
 
 int decode_heads_per_wave(int G, int head_dim) {
-    if (head_dim == 128) {  // matrix path: the largest divisor of G that is <= 16
+    if (head_dim == 128) {  // matrix path: 32 when G is a multiple of 32 (two column
+        if (G % 32 == 0) return 32;  // groups), else the largest divisor of G <= 16
         for (int gw = G < 16 ? G : 16; gw > 1; --gw)
             if (G % gw == 0) return gw;
         return 1;
@@ -871,10 +894,14 @@ hipError_t launch_decode(const StepArgs& a) {
     if (grid64 > INT32_MAX) return hipErrorInvalidValue;
     const int grid = (int)grid64;
     if (a.head_dim == 128) {
-        if (a.block_size == 16)
-            hipLaunchKernelGGL(decode_mfma_kernel<16>, dim3(grid), dim3(256), 0, a.stream, p);
-        else
-            hipLaunchKernelGGL(decode_mfma_kernel<4>, dim3(grid), dim3(256), 0, a.stream, p);
+        const bool two = GW > 16;  // 32 heads per wave: two MFMA column groups
+        if (a.block_size == 16) {
+            if (two) hipLaunchKernelGGL((decode_mfma_kernel<16, 2>), dim3(grid), dim3(256), 0, a.stream, p);
+            else hipLaunchKernelGGL((decode_mfma_kernel<16, 1>), dim3(grid), dim3(256), 0, a.stream, p);
+        } else {
+            if (two) hipLaunchKernelGGL((decode_mfma_kernel<4, 2>), dim3(grid), dim3(256), 0, a.stream, p);
+            else hipLaunchKernelGGL((decode_mfma_kernel<4, 1>), dim3(grid), dim3(256), 0, a.stream, p);
+        }
     } else {
         if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);
         else launch_decode_gw<16, 4>(a, p, GW, grid);

@@ -44,6 +44,8 @@ WORKLOADS = {
                    "context U{512..4096}, block 16", W.decode_mha),
     "decode_gqa": ("GQA decode: 256 sequences, 32/8 heads, head_dim 128, context lognormal "
                    "(median 1024, sigma 0.8, clip [16, 8192]), block 16", W.decode_gqa),
+    "decode_mqa": ("MQA decode: 256 sequences, 32 q heads on 1 kv head, head_dim 128, context "
+                   "lognormal (median 4096, sigma 0.8, clip [64, 32768]), block 16", W.decode_mqa),
     "long_prefill": ("32768-token prompt as 16 sequential 2048-token chunks; 32/8 heads, "
                      "head_dim 128, block 16", W.long_prefill),
     "shared_prefix": ("16 x 256-token suffix chunks over one shared 2048-token prefix; "

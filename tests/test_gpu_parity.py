@@ -41,6 +41,11 @@ SMALL = [
     ("decode_gqa4", [(c, 1) for c in DEC_LENS], 8, 2, 128, 16),
     ("decode_gqa8", [(c, 1) for c in DEC_LENS], 16, 2, 128, 16),
     ("decode_gqa16", [(c, 1) for c in DEC_LENS], 16, 1, 128, 16),
+    # MQA / large group ratios: one wave carries 32 q heads as two MFMA column groups
+    ("decode_mqa32", [(c, 1) for c in DEC_LENS], 32, 1, 128, 16),
+    ("decode_g32_bs4", [(c, 1) for c in DEC_LENS], 64, 2, 128, 4),
+    ("decode_g64", [(c, 1) for c in DEC_LENS[:9]], 64, 1, 128, 16),
+    ("mixed_mqa32", MIXED_SPECS, 32, 1, 128, 16),
     ("prefill_mha", PRE_SPECS, 2, 2, 128, 16),
     ("prefill_gqa2", PRE_SPECS, 4, 2, 128, 16),
     ("prefill_gqa4_bs4", PRE_SPECS, 8, 2, 128, 4),

@@ -252,6 +252,16 @@ def decode_gqa(seed: int = 2, num_seqs: int = 256) -> Workload:
                               num_kv_heads=8, head_dim=128, block_size=16, seed=seed, rng=rng)
 
 
+def decode_mqa(seed: int = 5, num_seqs: int = 256) -> Workload:
+    """MQA decode (one kv head for all 32 q heads, 1/32 of the MHA cache per
+    token): 32/1 heads, A=128, bs=16, context lognormal with median 4096 and
+    sigma 0.8, rounded and clipped to [64, 32768]."""
+    rng = np.random.default_rng(seed)
+    ctx = np.clip(np.rint(np.exp(rng.normal(math.log(4096.0), 0.8, size=num_seqs))), 64, 32768)
+    return make_step_workload("decode_mqa", [(int(c), 1) for c in ctx], num_q_heads=32,
+                              num_kv_heads=1, head_dim=128, block_size=16, seed=seed, rng=rng)
+
+
 def mixed(seed: int = 3, num_decode: int = 512, chunk: int = 512,
           chunk_ctx=(0, 512, 1024, 3584)) -> Workload:
     """Mixed continuous-batching step, token budget 2560: 4 prefill chunks of

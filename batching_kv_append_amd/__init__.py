@@ -50,6 +50,10 @@ _sig("kvc_num_blocks", _I32, [_P])
 _sig("kvc_block_refcount", _I32, [_P, _I32])
 _sig("kvc_extend_table", ctypes.c_int, [_P, _P, _I32, ctypes.POINTER(_I32), _I64])
 _sig("kvc_cache_bytes", _I64, [_I64, _I32, _I32, _I32, _I32])
+_sig("kvc_cow_block", ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)])
+_sig("kvc_fork_table", ctypes.c_int,
+     [_P, _P, _I64, _P, _I32, ctypes.POINTER(_I32), _P, _P, ctypes.POINTER(_I32)])
+_sig("kvc_copy_blocks", ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P])
 _sig("kvc_append_kv", ctypes.c_int,
      [_P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P])
 _sig("kvc_gather_kv", ctypes.c_int,
@@ -73,6 +77,7 @@ EXPORTED = [
     "kvc_status_string", "kvc_last_error", "kvc_allocator_create", "kvc_allocator_destroy",
     "kvc_alloc_blocks", "kvc_share_blocks", "kvc_free_blocks", "kvc_num_free_blocks",
     "kvc_num_blocks", "kvc_block_refcount", "kvc_extend_table", "kvc_cache_bytes",
+    "kvc_cow_block", "kvc_fork_table", "kvc_copy_blocks",
     "kvc_append_kv", "kvc_gather_kv", "kvc_workspace_size", "kvc_paged_attention_varlen",
     "kvc_workspace_flags", "kvc_profile_begin", "kvc_profile_end",
 ]
@@ -200,6 +205,35 @@ def kvc_extend_table(alloc: Allocator, row, held: int, new_len: int) -> int:
     return int(h.value)
 
 
+def kvc_cow_block(alloc: Allocator, block_id: int):
+    """Copy-on-write before writing into block_id: returns (id to write,
+    copied); when copied is True the caller copies the old block's contents
+    (kvc_copy_blocks) into the returned one first."""
+    out, copied = _I32(0), _I32(0)
+    _check(_lib.kvc_cow_block(alloc.handle, block_id, ctypes.byref(out), ctypes.byref(copied)),
+           "kvc_cow_block")
+    return int(out.value), bool(copied.value)
+
+
+def kvc_fork_table(alloc: Allocator, parent_row, length: int, child_row):
+    """Fork: child_row (int32 numpy array, written in place) takes the
+    parent's first ceil(length / block_size) blocks, sharing the full ones and
+    copying a partially filled last one on write.  Returns (held, copies) with
+    copies a list of (src, dst) block pairs for kvc_copy_blocks."""
+    import numpy as np
+    for name, r in (("parent_row", parent_row), ("child_row", child_row)):
+        if not (isinstance(r, np.ndarray) and r.dtype == np.int32 and r.flags["C_CONTIGUOUS"]):
+            raise TypeError(f"{name}: expected a C-contiguous int32 numpy array")
+    src, dst = np.zeros(1, np.int32), np.zeros(1, np.int32)
+    held, n = _I32(0), _I32(0)
+    _check(_lib.kvc_fork_table(alloc.handle, parent_row.ctypes.data_as(ctypes.c_void_p), length,
+                               child_row.ctypes.data_as(ctypes.c_void_p), child_row.size,
+                               ctypes.byref(held), src.ctypes.data_as(ctypes.c_void_p),
+                               dst.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)),
+           "kvc_fork_table")
+    return int(held.value), [(int(src[0]), int(dst[0]))] if n.value else []
+
+
 def kvc_cache_bytes(num_blocks, block_size, num_kv_heads, head_dim, elem_bytes=2) -> int:
     return int(_lib.kvc_cache_bytes(num_blocks, block_size, num_kv_heads, head_dim, elem_bytes))
 
@@ -251,6 +285,18 @@ def kvc_gather_kv(k_cache, v_cache, block_table, seq_lens, cu_seq_lens, k_out, v
                               block_table.shape[1], _ptr(seq_lens), _ptr(cu_seq_lens),
                               k_out.shape[0], _ptr(k_out), _ptr(v_out), s, hkv, a, bs,
                               _stream(stream)), "kvc_gather_kv")
+
+
+def kvc_copy_blocks(k_cache, v_cache, src_ids, dst_ids, stream=None):
+    """Block dst_ids[i] := block src_ids[i] in both pools (int32 GPU tensors)."""
+    nb, hkv, bs, a = _cache_dims(k_cache, v_cache)
+    _need(src_ids, torch.int32, 1, "src_ids")
+    _need(dst_ids, torch.int32, 1, "dst_ids")
+    if src_ids.shape != dst_ids.shape:
+        raise ValueError("src_ids and dst_ids must have the same length")
+    _check(_lib.kvc_copy_blocks(_ptr(k_cache), _ptr(v_cache), nb, _ptr(src_ids), _ptr(dst_ids),
+                                src_ids.shape[0], hkv, a, bs, _stream(stream)),
+           "kvc_copy_blocks")
 
 
 def kvc_workspace_size(num_seqs, total_q, max_q_len, max_context_len, num_q_heads,

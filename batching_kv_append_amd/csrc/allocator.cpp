@@ -146,6 +146,65 @@ extern "C" int kvc_extend_table(kvc_allocator* a, int32_t* row, int32_t max_bloc
     return KVC_OK;
 }
 
+// Copy-on-write.  Sharing is done by editing tables (klklkl10086.github.io
+// kv_cache post, section "Paged Attention"), and a contiguous cache cannot
+// share at all (same post, section "连续内存分配", beam search).  A shared block
+// that one sharer is about to write into is first copied, so the others keep
+// their contents: the writer takes a fresh block, drops its reference to the
+// shared one, and copies the contents on the device (kvc_copy_blocks).
+extern "C" int kvc_cow_block(kvc_allocator* a, int32_t id, int32_t* out_id, int32_t* copied) {
+    if (!a || !out_id || !copied) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_cow_block: NULL argument");
+    if (!valid_id(a, id) || a->refcount[id] <= 0)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_cow_block: id out of range or free");
+    if (a->refcount[id] == 1) {  // sole owner: write in place
+        *out_id = id;
+        *copied = 0;
+        return KVC_OK;
+    }
+    if (a->free_stack.empty()) return kvc_fail(KVC_ERR_OOM, "kvc_cow_block: no free block");
+    const int32_t nid = a->free_stack.back();
+    a->free_stack.pop_back();
+    a->refcount[nid] = 1;
+    --a->refcount[id];  // > 0: other sharers remain
+    *out_id = nid;
+    *copied = 1;
+    return KVC_OK;
+}
+
+extern "C" int kvc_fork_table(kvc_allocator* a, const int32_t* parent_row, int64_t len,
+                              int32_t* child_row, int32_t max_blocks, int32_t* child_held,
+                              int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies) {
+    if (!a || !parent_row || !child_row || !child_held || !copy_src || !copy_dst || !n_copies)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_fork_table: NULL argument");
+    if (len < 0 || max_blocks < 0) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_fork_table: bad sizes");
+    const int64_t nb = (len + a->block_size - 1) / a->block_size;
+    if (nb > max_blocks) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_fork_table: row too short for len");
+    const bool partial = len % a->block_size != 0;
+    const int32_t full = (int32_t)(partial ? nb - 1 : nb);
+    for (int32_t i = 0; i < nb; ++i)
+        if (!valid_id(a, parent_row[i]) || a->refcount[parent_row[i]] <= 0)
+            return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_fork_table: parent id out of range or free");
+    if (partial && a->free_stack.empty()) return kvc_fail(KVC_ERR_OOM, "kvc_fork_table: no free block");
+    int rc = kvc_share_blocks(a, parent_row, full);  // all or nothing by itself
+    if (rc != KVC_OK) return rc;
+    for (int32_t i = 0; i < full; ++i) child_row[i] = parent_row[i];
+    *n_copies = 0;
+    if (partial) {  // the child will write into the last block: its own copy
+        int32_t nid = 0;
+        rc = kvc_alloc_blocks(a, 1, &nid);  // cannot fail: checked above
+        if (rc != KVC_OK) {
+            for (int32_t i = 0; i < full; ++i) --a->refcount[parent_row[i]];
+            return rc;
+        }
+        child_row[full] = nid;
+        copy_src[0] = parent_row[full];
+        copy_dst[0] = nid;
+        *n_copies = 1;
+    }
+    *child_held = (int32_t)nb;
+    return KVC_OK;
+}
+
 extern "C" int64_t kvc_cache_bytes(int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t elem_bytes) {
     if (num_blocks < 0 || block_size < 0 || num_kv_heads < 0 || head_dim < 0 || elem_bytes < 0)

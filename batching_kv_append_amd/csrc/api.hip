@@ -13,6 +13,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <algorithm>
 #include <vector>
 
 #include "kvc.h"
@@ -256,6 +257,43 @@ extern "C" int kvc_gather_kv(const void* k_cache, const void* v_cache, int64_t n
     hipError_t e = kvc::launch_gather(k_cache, v_cache, num_blocks, block_table, max_blocks_per_seq,
                                       seq_lens, cu_seq_lens, total_tokens, k_out, v_out, num_seqs,
                                       num_kv_heads, head_dim, block_size, (hipStream_t)stream);
+    return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
+}
+
+extern "C" int kvc_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
+                               const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               void* stream) {
+    const char* fn = "kvc_copy_blocks";
+    if (n < 0) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_copy_blocks: negative count");
+    if (int rc = check_kv_shape(num_kv_heads, head_dim, block_size, fn)) return rc;
+    if (n == 0) return KVC_OK;
+    if (!k_cache || !v_cache || !src_ids || !dst_ids)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_copy_blocks: NULL pointer");
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_copy_blocks: K/V pointers must be 16-byte aligned");
+    if (num_blocks < 1) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_copy_blocks: num_blocks must be >= 1");
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_mode()) {  // ids in range, destinations distinct and not sources
+        std::vector<int32_t> src(n), dst(n);
+        hipError_t e = hipMemcpyAsync(src.data(), src_ids, (size_t)n * 4, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipMemcpyAsync(dst.data(), dst_ids, (size_t)n * 4, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "KVC_DEBUG check");
+        std::vector<int32_t> seen(dst);
+        std::sort(seen.begin(), seen.end());
+        for (int32_t i = 0; i < n; ++i) {
+            if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks)
+                return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: block id out of range");
+            if (i > 0 && seen[i] == seen[i - 1])
+                return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: repeated destination block");
+        }
+        for (int32_t i = 0; i < n; ++i)
+            if (std::binary_search(seen.begin(), seen.end(), src[i]))
+                return kvc_fail(KVC_ERR_INVALID_ARG, "KVC_DEBUG: a destination is also a source");
+    }
+    hipError_t e = kvc::launch_copy_blocks(k_cache, v_cache, num_blocks, src_ids, dst_ids, n,
+                                           num_kv_heads, head_dim, block_size, st);
     return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
 }
 

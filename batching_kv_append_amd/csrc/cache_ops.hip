@@ -61,7 +61,31 @@ __global__ __launch_bounds__(256) void gather_kernel(
     }
 }
 
+// Block copy for copy-on-write: workgroup (i, pool) copies block src[i] of
+// that pool to block dst[i] (all kv heads and slots), 16 bytes per thread
+// per step.  A pair with an id outside [0, num_blocks) is skipped.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int64_t num_blocks,
+    const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int64_t block_chunks) {
+    const int64_t s = src[blockIdx.x], d = dst[blockIdx.x];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+    uint4* pool = blockIdx.y == 0 ? k_cache : v_cache;
+    const uint4* from = pool + s * block_chunks;
+    uint4* to = pool + d * block_chunks;
+    for (int64_t c = threadIdx.x; c < block_chunks; c += 256) to[c] = from[c];
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
+                              const int32_t* src, const int32_t* dst, int32_t n, int32_t hkv,
+                              int32_t head_dim, int32_t block_size, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t block_chunks = (int64_t)hkv * block_size * (head_dim / 8);
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n, 2), dim3(256), 0, stream,
+                       (uint4*)k_cache, (uint4*)v_cache, num_blocks, src, dst, block_chunks);
+    return hipGetLastError();
+}
 
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          int64_t num_blocks, const int32_t* table, int32_t max_blocks,

@@ -43,6 +43,9 @@ hipError_t launch_gather(const void* k_cache, const void* v_cache, int64_t num_b
 
 // One launch: work lists for the decode and prefill kernels (zeroes the
 // header flags) and, with_append, the append of k_new / v_new.
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
+                              const int32_t* src, const int32_t* dst, int32_t n, int32_t hkv,
+                              int32_t head_dim, int32_t block_size, hipStream_t stream);
 hipError_t launch_prep(const StepArgs& a, bool with_append);
 // Split-K decode partials (+ direct output for one-partition sequences).
 hipError_t launch_decode(const StepArgs& a);

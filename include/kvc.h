@@ -135,6 +135,29 @@ int32_t kvc_block_refcount(const kvc_allocator* a, int32_t id);
 int kvc_extend_table(kvc_allocator* a, int32_t* row, int32_t max_blocks,
                      int32_t* held, int64_t new_len);
 
+/* Copy-on-write of one block before a write into it (a shared block must
+ * not change under its other sharers; sharing by table edits, klklkl10086
+ * kv_cache post, sections "Paged Attention" and "连续内存分配").  If `id` has
+ * one reference, *out_id = id and *copied = 0.  Otherwise a fresh block is
+ * taken (refcount 1), one reference to `id` is dropped, *out_id is the new
+ * block and *copied = 1: the caller copies the contents (kvc_copy_blocks)
+ * before writing.  KVC_ERR_OOM (no free block) or KVC_ERR_INVALID_ARG (free
+ * or out-of-range id) leave everything unchanged. */
+int kvc_cow_block(kvc_allocator* a, int32_t id, int32_t* out_id, int32_t* copied);
+
+/* Fork a sequence (a shared prefix or a beam): the child's table row takes the
+ * parent's first ceil(len / block_size) blocks.  Full blocks are shared (one
+ * more reference each); a partially filled last block (len % block_size != 0),
+ * which the child will append into, is copied on write: the child gets a
+ * fresh block and (copy_src[0], copy_dst[0]) = (parent's block, new block),
+ * *n_copies = 1, for kvc_copy_blocks (else *n_copies = 0).  *child_held =
+ * ceil(len / block_size).  All or nothing: KVC_ERR_OOM / KVC_ERR_INVALID_ARG
+ * (row longer than max_blocks, a free or out-of-range parent id) change
+ * nothing. */
+int kvc_fork_table(kvc_allocator* a, const int32_t* parent_row, int64_t len,
+                   int32_t* child_row, int32_t max_blocks, int32_t* child_held,
+                   int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies);
+
 /* Bytes of the two pools (K and V): 2 * num_blocks * block_size *
  * num_kv_heads * head_dim * elem_bytes.  Per token and layer this is the
  * 2*H*A values of the cache-size formula.  Returns -1 on a negative input. */
@@ -166,6 +189,15 @@ int kvc_gather_kv(const void* k_cache, const void* v_cache, int64_t num_blocks,
                   const int32_t* seq_lens, const int64_t* cu_seq_lens, int64_t total_tokens,
                   void* k_out, void* v_out, int32_t num_seqs, int32_t num_kv_heads,
                   int32_t head_dim, int32_t block_size, void* stream);
+
+/* Block copy for copy-on-write: block dst_ids[i] := block src_ids[i] in both
+ * pools (all kv heads and slots), i < n.  src_ids, dst_ids: device int32
+ * arrays.  A pair with an id outside [0, num_blocks) is skipped (KVC_DEBUG=1
+ * checks on the host and rejects it).  The destinations must be distinct and
+ * must not be among the sources (the copies run concurrently).  Bit copy. */
+int kvc_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks, const int32_t* src_ids,
+                    const int32_t* dst_ids, int32_t n, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, void* stream);
 
 /* Workspace bytes kvc_paged_attention_varlen needs for a step with these
  * bounds (max_context_len >= every context_lens[s], max_q_len >= every

@@ -64,7 +64,7 @@ int main() {
     std::mt19937 rng(1);
     std::vector<int32_t> live;
     for (int it = 0; it < 20000; ++it) {
-        int op = rng() % 3;
+        int op = rng() % 4;
         if (op == 0) {
             int32_t n = rng() % 5;
             std::vector<int32_t> got(n + 1);
@@ -79,6 +79,21 @@ int main() {
             int32_t id = live[rng() % live.size()];
             CHECK(kvc_share_blocks(a, &id, 1) == KVC_OK);
             live.push_back(id);
+        } else if (op == 2 && !live.empty()) {  // copy-on-write of one held reference
+            size_t k = rng() % live.size();
+            int32_t nid = -1, copied = -1;
+            const int32_t rc0 = kvc_block_refcount(a, live[k]);
+            const int free0 = kvc_num_free_blocks(a);
+            int rc = kvc_cow_block(a, live[k], &nid, &copied);
+            if (rc0 == 1) {
+                CHECK(rc == KVC_OK && nid == live[k] && copied == 0);
+            } else if (free0 == 0) {
+                CHECK(rc == KVC_ERR_OOM && kvc_block_refcount(a, live[k]) == rc0);
+            } else {
+                CHECK(rc == KVC_OK && copied == 1 && nid != live[k]);
+                CHECK(kvc_block_refcount(a, live[k]) == rc0 - 1 && kvc_block_refcount(a, nid) == 1);
+                live[k] = nid;  // the reference moved to the copy
+            }
         } else if (!live.empty()) {
             size_t k = rng() % live.size();
             int32_t id = live[k];
@@ -88,6 +103,19 @@ int main() {
         }
         if (it % 1000 == 0) invariants(a);
     }
+    kvc_allocator_destroy(a);
+    // fork of a 40-token row (block 16): 2 shared + 1 copied block
+    CHECK(kvc_allocator_create(8, 16, &a) == KVC_OK);
+    std::vector<int32_t> parent(4, -1), child(4, -1);
+    int32_t ph = 0, chh = 0, src = -1, dst = -1, nc = -1;
+    CHECK(kvc_extend_table(a, parent.data(), 4, &ph, 40) == KVC_OK && ph == 3);
+    CHECK(kvc_fork_table(a, parent.data(), 40, child.data(), 4, &chh, &src, &dst, &nc) == KVC_OK);
+    CHECK(chh == 3 && nc == 1 && src == parent[2] && dst == child[2] && child[0] == parent[0]);
+    CHECK(kvc_block_refcount(a, parent[0]) == 2 && kvc_block_refcount(a, parent[2]) == 1);
+    CHECK(kvc_fork_table(a, parent.data(), 40, child.data(), 2, &chh, &src, &dst, &nc) == KVC_ERR_INVALID_ARG);
+    CHECK(kvc_free_blocks(a, parent.data(), 3) == KVC_OK && kvc_free_blocks(a, child.data(), 3) == KVC_OK);
+    CHECK(kvc_num_free_blocks(a) == 8);
+    invariants(a);
     kvc_allocator_destroy(a);
     kvc_allocator_destroy(nullptr);
     CHECK(kvc_cache_bytes(1, 1, 32, 128, 2) == 16384);

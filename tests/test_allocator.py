@@ -71,6 +71,74 @@ def test_prefix_sharing_footprint(kvc):
     assert kvc.kvc_num_free_blocks(a) == 4096
 
 
+def test_copy_on_write(kvc):
+    """A block with one owner is written in place; a shared one is replaced by
+    a fresh block for the writer, and the other sharers keep theirs."""
+    a = kvc.Allocator(4, 16)
+    (b,) = kvc.kvc_alloc_blocks(a, 1)
+    assert kvc.kvc_cow_block(a, b) == (b, False)
+    kvc.kvc_share_blocks(a, [b])
+    nb, copied = kvc.kvc_cow_block(a, b)
+    assert copied and nb != b
+    assert kvc.kvc_block_refcount(a, b) == 1 and kvc.kvc_block_refcount(a, nb) == 1
+    assert kvc.kvc_num_free_blocks(a) == 2
+    for bad in (-1, 4, 3):  # out of range, out of range, free
+        with pytest.raises(kvc.KvcError) as e:
+            kvc.kvc_cow_block(a, bad)
+        assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+    # no free block: OOM and nothing changes
+    kvc.kvc_alloc_blocks(a, 2)
+    kvc.kvc_share_blocks(a, [b])
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_cow_block(a, b)
+    assert e.value.status == kvc.KVC_ERR_OOM and kvc.kvc_block_refcount(a, b) == 2
+
+
+@pytest.mark.parametrize("length", [0, 1, 15, 16, 17, 37, 48])
+def test_fork_table(kvc, length):
+    """Fork of a sequence holding `length` tokens (block size 16): full blocks
+    shared, a partial last block copied on write, all or nothing."""
+    a = kvc.Allocator(16, 16)
+    parent = np.full(4, -1, dtype=np.int32)
+    held = kvc.kvc_extend_table(a, parent, 0, length)
+    free0 = kvc.kvc_num_free_blocks(a)
+    child = np.full(4, -1, dtype=np.int32)
+    ch, copies = kvc.kvc_fork_table(a, parent, length, child)
+    nb = -(-length // 16)
+    full = length // 16
+    assert ch == nb == held
+    assert child[:full].tolist() == parent[:full].tolist()
+    for i in range(full):
+        assert kvc.kvc_block_refcount(a, int(parent[i])) == 2
+    if length % 16:
+        assert copies == [(int(parent[full]), int(child[full]))]
+        assert child[full] != parent[full]
+        assert kvc.kvc_block_refcount(a, int(parent[full])) == 1
+        assert kvc.kvc_block_refcount(a, int(child[full])) == 1
+        assert kvc.kvc_num_free_blocks(a) == free0 - 1
+    else:
+        assert copies == [] and kvc.kvc_num_free_blocks(a) == free0
+    # freeing both tables returns every block
+    kvc.kvc_free_blocks(a, parent[:held])
+    kvc.kvc_free_blocks(a, child[:ch])
+    assert kvc.kvc_num_free_blocks(a) == 16
+
+
+def test_fork_table_all_or_nothing(kvc):
+    a = kvc.Allocator(3, 16)
+    parent = np.full(4, -1, dtype=np.int32)
+    kvc.kvc_extend_table(a, parent, 0, 40)  # 3 blocks, the last one partial
+    child = np.full(4, -1, dtype=np.int32)
+    with pytest.raises(kvc.KvcError) as e:  # the copy needs a free block
+        kvc.kvc_fork_table(a, parent, 40, child)
+    assert e.value.status == kvc.KVC_ERR_OOM
+    assert [kvc.kvc_block_refcount(a, int(i)) for i in parent[:3]] == [1, 1, 1]
+    with pytest.raises(kvc.KvcError) as e:  # child row too short
+        kvc.kvc_fork_table(a, parent, 32, np.full(1, -1, dtype=np.int32))
+    assert e.value.status == kvc.KVC_ERR_INVALID_ARG
+    assert [kvc.kvc_block_refcount(a, int(i)) for i in parent[:3]] == [1, 1, 1]
+
+
 def test_native_driver_under_sanitizers(tmp_path):
     exe = tmp_path / "allocator_driver"
     srcs = [os.path.join(ROOT, "tests", "native", "allocator_driver.cpp"),

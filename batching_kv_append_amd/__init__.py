@@ -50,7 +50,17 @@ _sig("kvc_num_blocks", _I32, [_P])
 _sig("kvc_block_refcount", _I32, [_P, _I32])
 _sig("kvc_extend_table", ctypes.c_int, [_P, _P, _I32, ctypes.POINTER(_I32), _I64])
 _sig("kvc_cache_bytes", _I64, [_I64, _I32, _I32, _I32, _I32])
+_sig("kvc_allocator_block_size", _I32, [_P])
 _sig("kvc_cow_block", ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)])
+_sig("kvc_scheduler_create", ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.POINTER(_P)])
+_sig("kvc_scheduler_destroy", None, [_P])
+_sig("kvc_scheduler_add", ctypes.c_int, [_P, _I64, _I32, _I32])
+_sig("kvc_scheduler_step", ctypes.c_int,
+     [_P, _P, _P, _P, _P, ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+      ctypes.POINTER(_I32)])
+_sig("kvc_scheduler_complete", ctypes.c_int, [_P, _P, ctypes.POINTER(_I32)])
+_sig("kvc_scheduler_num_waiting", _I32, [_P])
+_sig("kvc_scheduler_num_running", _I32, [_P])
 _sig("kvc_fork_table", ctypes.c_int,
      [_P, _P, _I64, _P, _I32, ctypes.POINTER(_I32), _P, _P, ctypes.POINTER(_I32)])
 _sig("kvc_copy_blocks", ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P])
@@ -77,7 +87,9 @@ EXPORTED = [
     "kvc_status_string", "kvc_last_error", "kvc_allocator_create", "kvc_allocator_destroy",
     "kvc_alloc_blocks", "kvc_share_blocks", "kvc_free_blocks", "kvc_num_free_blocks",
     "kvc_num_blocks", "kvc_block_refcount", "kvc_extend_table", "kvc_cache_bytes",
-    "kvc_cow_block", "kvc_fork_table", "kvc_copy_blocks",
+    "kvc_cow_block", "kvc_fork_table", "kvc_copy_blocks", "kvc_allocator_block_size",
+    "kvc_scheduler_create", "kvc_scheduler_destroy", "kvc_scheduler_add", "kvc_scheduler_step",
+    "kvc_scheduler_complete", "kvc_scheduler_num_waiting", "kvc_scheduler_num_running",
     "kvc_append_kv", "kvc_gather_kv", "kvc_workspace_size", "kvc_paged_attention_varlen",
     "kvc_workspace_flags", "kvc_profile_begin", "kvc_profile_end",
 ]
@@ -203,6 +215,89 @@ def kvc_extend_table(alloc: Allocator, row, held: int, new_len: int) -> int:
     _check(_lib.kvc_extend_table(alloc.handle, row.ctypes.data_as(ctypes.c_void_p), row.size,
                                  ctypes.byref(h), new_len), "kvc_extend_table")
     return int(h.value)
+
+
+def kvc_allocator_block_size(alloc: Allocator) -> int:
+    return int(_lib.kvc_allocator_block_size(alloc.handle))
+
+
+class StepPlan:
+    """Host arrays of one planned step (numpy views sized to the step)."""
+
+    def __init__(self, cu_seqlens_q, context_lens, block_table, request_ids, max_q_len,
+                 max_context_len):
+        self.cu_seqlens_q = cu_seqlens_q
+        self.context_lens = context_lens
+        self.block_table = block_table
+        self.request_ids = request_ids
+        self.max_q_len = max_q_len
+        self.max_context_len = max_context_len
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+
+class Scheduler:
+    """Host continuous-batching scheduler over an Allocator (kvc_scheduler_*)."""
+
+    def __init__(self, alloc: Allocator, token_budget: int, max_seqs: int, max_blocks_per_seq: int):
+        import numpy as np
+        h = _P()
+        _check(_lib.kvc_scheduler_create(alloc.handle, token_budget, max_seqs, max_blocks_per_seq,
+                                         ctypes.byref(h)), "kvc_scheduler_create")
+        self._h, self._alloc = h, alloc  # keeps the allocator alive
+        self.max_seqs, self.max_blocks = max_seqs, max_blocks_per_seq
+        self._cu = np.zeros(max_seqs + 1, np.int32)
+        self._ctx = np.zeros(max_seqs, np.int32)
+        self._table = np.zeros((max_seqs, max_blocks_per_seq), np.int32)
+        self._ids = np.zeros(max_seqs, np.int64)
+        self._fin = np.zeros(max_seqs, np.int64)
+
+    def close(self):
+        if self._h:
+            _lib.kvc_scheduler_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, request_id: int, prompt_len: int, max_new_tokens: int):
+        _check(_lib.kvc_scheduler_add(self._h, request_id, prompt_len, max_new_tokens),
+               "kvc_scheduler_add")
+
+    def step(self) -> StepPlan:
+        """Plan the next step; the returned arrays are views valid until the next step."""
+        n, t, mq, mc = _I32(0), _I32(0), _I32(0), _I32(0)
+        p = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        _check(_lib.kvc_scheduler_step(self._h, p(self._cu), p(self._ctx), p(self._table),
+                                       p(self._ids), ctypes.byref(n), ctypes.byref(t),
+                                       ctypes.byref(mq), ctypes.byref(mc)), "kvc_scheduler_step")
+        k = int(n.value)
+        return StepPlan(self._cu[:k + 1], self._ctx[:k], self._table[:k], self._ids[:k],
+                        int(mq.value), int(mc.value))
+
+    def complete(self):
+        """Mark the planned step as executed; returns the finished request ids."""
+        n = _I32(0)
+        _check(_lib.kvc_scheduler_complete(self._h, self._fin.ctypes.data_as(ctypes.c_void_p),
+                                           ctypes.byref(n)), "kvc_scheduler_complete")
+        return self._fin[:n.value].tolist()
+
+    @property
+    def num_waiting(self) -> int:
+        return int(_lib.kvc_scheduler_num_waiting(self._h))
+
+    @property
+    def num_running(self) -> int:
+        return int(_lib.kvc_scheduler_num_running(self._h))
 
 
 def kvc_cow_block(alloc: Allocator, block_id: int):

@@ -125,6 +125,10 @@ extern "C" int32_t kvc_num_blocks(const kvc_allocator* a) {
     return a ? (int32_t)a->refcount.size() : -1;
 }
 
+extern "C" int32_t kvc_allocator_block_size(const kvc_allocator* a) {
+    return a ? a->block_size : -1;
+}
+
 extern "C" int32_t kvc_block_refcount(const kvc_allocator* a, int32_t id) {
     if (!a || !valid_id(a, id)) return -1;
     return a->refcount[id];

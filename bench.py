@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import platform
 import sys
@@ -51,6 +52,137 @@ WORKLOADS = {
     "shared_prefix": ("16 x 256-token suffix chunks over one shared 2048-token prefix; "
                       "32/8 heads, head_dim 128, block 16", W.shared_prefix),
 }
+
+
+SERVE_DESC = ("continuous-batching serve loop: host scheduler (token budget 2560 rows, <= 1024 "
+              "sequences per step) over a seeded trace of 4096 requests, prompts U{128..4096}, "
+              "new tokens U{32..512}; 32 q / 8 kv heads, head_dim 128, bf16, block 16; one "
+              "layer's attention per step")
+
+
+def run_serve(args, kvc):
+    """Sustained throughput of scheduler-driven steps: every step the host
+    scheduler plans the rows (decode rows, prompt chunks, admissions, blocks
+    just in time), the plan is copied into one of two device buffer sets, and
+    the library runs the step; planning the next step overlaps the GPU."""
+    budget, max_seqs, bs, hq, hkv, a = 2560, 1024, 16, 32, 8, 128
+    n_req, max_prompt, max_new = 4096, 4096, 512
+    rng = np.random.default_rng(6 if args.seed is None else args.seed)
+    prompts = rng.integers(128, max_prompt, n_req, endpoint=True)
+    news = rng.integers(32, max_new, n_req, endpoint=True)
+    mb = -(-(max_prompt + max_new) // bs)
+    nb = 131072  # 8.6 GB of K/V pool
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    alloc = kvc.Allocator(nb, bs)
+    sched = kvc.Scheduler(alloc, budget, max_seqs, mb)
+    for i in range(n_req):
+        sched.add(i, int(prompts[i]), int(news[i]))
+    g = torch.Generator(device="cuda").manual_seed(0)
+    k_cache = torch.randn(nb, hkv, bs, a, generator=g, device="cuda").to(torch.bfloat16)
+    v_cache = torch.randn(nb, hkv, bs, a, generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn(budget, hq, a, generator=g, device="cuda").to(torch.bfloat16)
+    kn = torch.randn(budget, hkv, a, generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(budget, hkv, a, generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = kvc.new_workspace(max_seqs, budget, budget, max_prompt + max_new, hq, hkv, a, bs)
+    scale = 1.0 / math.sqrt(a)
+    # two buffer sets: step i uses set i % 2 once step i - 2 has finished with it
+    pin = [dict(cu=torch.empty(max_seqs + 1, dtype=torch.int32).pin_memory(),
+                ctx=torch.empty(max_seqs, dtype=torch.int32).pin_memory(),
+                table=torch.empty(max_seqs, mb, dtype=torch.int32).pin_memory()) for _ in range(2)]
+    dev = [{k: torch.empty(v.shape, dtype=torch.int32, device="cuda") for k, v in b.items()}
+           for b in pin]
+    done = [torch.cuda.Event() for _ in range(2)]
+    state = dict(i=0, finished=0)
+    alg = dict(tokens=0, decode_rows=0, decode_bytes=0, pairs=0)
+
+    def one_step():
+        p = sched.step()
+        if p.num_seqs == 0:
+            return False
+        k = state["i"] % 2
+        done[k].synchronize()
+        n, t = p.num_seqs, p.total_q
+        pin[k]["cu"][:n + 1].numpy()[:] = p.cu_seqlens_q
+        pin[k]["ctx"][:n].numpy()[:] = p.context_lens
+        pin[k]["table"][:n].numpy()[:] = p.block_table
+        for key, m in (("cu", n + 1), ("ctx", n), ("table", n)):
+            dev[k][key][:m].copy_(pin[k][key][:m], non_blocking=True)
+        kvc.kvc_paged_attention_varlen(out[:t], q[:t], kn[:t], vn[:t], k_cache, v_cache,
+                                       dev[k]["table"][:n], dev[k]["cu"][:n + 1], dev[k]["ctx"][:n],
+                                       scale, max_q_len=p.max_q_len,
+                                       max_context_len=p.max_context_len, workspace=ws,
+                                       stream=stream)
+        done[k].record(stream)
+        ql = np.diff(p.cu_seqlens_q).astype(np.int64)
+        c = p.context_lens.astype(np.int64)
+        alg["tokens"] += t
+        d = ql == 1  # decode rows, and one-row chunks, read like decode rows
+        alg["decode_rows"] += int(d.sum())
+        alg["decode_bytes"] += int((c[d] + 1).sum()) * hkv * a * 2 * 2
+        pr = ql >= 2
+        alg["pairs"] += int((ql[pr] * c[pr] + ql[pr] * (ql[pr] + 1) // 2).sum())
+        state["finished"] += len(sched.complete())
+        state["i"] += 1
+        return True
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    assert kvc.kvc_workspace_flags(ws) == 0
+    for key in alg:
+        alg[key] = 0
+    fin0 = state["finished"]
+    t0 = time.perf_counter()
+    steps = 0
+    while steps < args.steps and one_step():
+        steps += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    headline = dict(alg)
+    fin = state["finished"] - fin0
+    # kernel durations: the next K steps with HIP events around every launch
+    for key in alg:
+        alg[key] = 0
+    kvc.kvc_profile_begin(args.steps)
+    steps2 = 0
+    while steps2 < args.steps and one_step():
+        steps2 += 1
+    torch.cuda.synchronize()
+    phase_ms, ncalls = kvc.kvc_profile_end()
+    dec_us = phase_ms["decode"] * 1e3 / max(steps2, 1)
+    pre_us = phase_ms["prefill"] * 1e3 / max(steps2, 1)
+    dec_bytes = alg["decode_bytes"] / max(steps2, 1)
+    pre_flops = 4 * a * hq * alg["pairs"] / max(steps2, 1)
+    if dec_us >= pre_us:
+        gbps = dec_bytes / (dec_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "decode_mfma_kernel (split-K partials)",
+                    "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                    "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_us": dec_us}
+    else:
+        tf = pre_flops / (pre_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA)", "achieved": tf,
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                    "algorithmic_flops_per_launch": pre_flops, "avg_launch_us": pre_us}
+    result = {
+        "metric": METRIC, "value": headline["tokens"] / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / max(steps, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded request trace; random K/V and rows)",
+        "config": {"workload": SERVE_DESC, "name": "serve", "requests": n_req,
+                   "token_budget": budget, "max_seqs": max_seqs, "num_q_heads": hq,
+                   "num_kv_heads": hkv, "head_dim": a, "block_size": bs, "pool_blocks": nb},
+        "roofline": roofline,
+        "serve": {"tokens_per_step": headline["tokens"] / max(steps, 1),
+                  "decode_rows_per_step": headline["decode_rows"] / max(steps, 1),
+                  "requests_finished_in_timed_steps": fin,
+                  "running_after": sched.num_running, "waiting_after": sched.num_waiting},
+        "kernels_us_per_step": {k: v * 1e3 / max(steps2, 1) for k, v in phase_ms.items()},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def dev_bits(a):
@@ -215,7 +347,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS) + ["serve"],
+                    help="serve: scheduler-driven steps over a request trace (use e.g. "
+                         "--steps 300 --warmup 300)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-every", type=int, default=2,
@@ -243,6 +377,9 @@ def main():
 
     import batching_kv_append_amd as kvc
 
+    if args.workload == "serve":
+        run_serve(args, kvc)
+        return
     desc, make = WORKLOADS[args.workload]
     t0 = time.perf_counter()
     wl = make() if args.seed is None else make(seed=args.seed)

@@ -123,6 +123,8 @@ int kvc_share_blocks(kvc_allocator* a, const int32_t* ids, int32_t n);
 int kvc_free_blocks(kvc_allocator* a, const int32_t* ids, int32_t n);
 int32_t kvc_num_free_blocks(const kvc_allocator* a);
 int32_t kvc_num_blocks(const kvc_allocator* a);
+/* Tokens per block the allocator was created with (-1 for NULL). */
+int32_t kvc_allocator_block_size(const kvc_allocator* a);
 /* Reference count of a block (0 = free), or -1 for an out-of-range id. */
 int32_t kvc_block_refcount(const kvc_allocator* a, int32_t id);
 
@@ -157,6 +159,49 @@ int kvc_cow_block(kvc_allocator* a, int32_t id, int32_t* out_id, int32_t* copied
 int kvc_fork_table(kvc_allocator* a, const int32_t* parent_row, int64_t len,
                    int32_t* child_row, int32_t max_blocks, int32_t* child_held,
                    int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies);
+
+/* ------------------------------------------------------------------------
+ * Host continuous-batching scheduler (news.myit.tw continuous-batching
+ * article, sections "Continuous batching" and "Chunked prefill"; blocks just
+ * in time, clvsit.github.io "PagedAttention 批处理").  Host memory only, not
+ * thread-safe.  Each step: one decode row per generating sequence (oldest
+ * first), then the next chunks of prompts in progress, then first-come
+ * first-served admissions, all within token_budget rows and max_seqs
+ * sequences.  On admission a request reserves the blocks of its whole life
+ * (ceil((prompt_len + max_new_tokens - 1) / block_size)); blocks are taken
+ * from the allocator when rows need them and returned when the request
+ * finishes, so an admitted request never runs out of blocks.  A prompt's last
+ * chunk produces its first token, each decode row the next one; a request
+ * finishes when it has produced max_new_tokens.
+ * ---------------------------------------------------------------------- */
+typedef struct kvc_scheduler kvc_scheduler;
+
+/* Create over an allocator (not owned; it must outlive the scheduler).
+ * token_budget >= 1 rows per step, max_seqs >= 1 sequences per step,
+ * max_blocks_per_seq >= 1 = the width of the block-table rows it writes. */
+int kvc_scheduler_create(kvc_allocator* alloc, int32_t token_budget, int32_t max_seqs,
+                         int32_t max_blocks_per_seq, kvc_scheduler** out);
+/* Destroy; blocks still held by running requests return to the allocator. */
+void kvc_scheduler_destroy(kvc_scheduler* s);
+/* Queue a request.  prompt_len, max_new_tokens >= 1; KVC_ERR_INVALID_ARG if
+ * it could never fit a table row or the pool. */
+int kvc_scheduler_add(kvc_scheduler* s, int64_t request_id, int32_t prompt_len,
+                      int32_t max_new_tokens);
+/* Plan the next step into host arrays with capacity max_seqs (+1 for
+ * cu_seqlens_q; block_table max_seqs * max_blocks_per_seq, entries past a
+ * row's held blocks are -1): the rows of sequence k are
+ * cu_seqlens_q[k] .. cu_seqlens_q[k+1]-1, cached before the step
+ * context_lens[k], request request_ids[k].  *num_seqs = 0 when nothing can
+ * run.  The table already covers the new rows.  A planned step must be
+ * completed before the next one is planned. */
+int kvc_scheduler_step(kvc_scheduler* s, int32_t* cu_seqlens_q, int32_t* context_lens,
+                       int32_t* block_table, int64_t* request_ids, int32_t* num_seqs,
+                       int32_t* total_q, int32_t* max_q_len, int32_t* max_context_len);
+/* Mark the planned step as executed: the sequences advance, finished requests
+ * (ids in finished_ids, capacity max_seqs, count *n_finished) free their blocks. */
+int kvc_scheduler_complete(kvc_scheduler* s, int64_t* finished_ids, int32_t* n_finished);
+int32_t kvc_scheduler_num_waiting(const kvc_scheduler* s);
+int32_t kvc_scheduler_num_running(const kvc_scheduler* s);
 
 /* Bytes of the two pools (K and V): 2 * num_blocks * block_size *
  * num_kv_heads * head_dim * elem_bytes.  Per token and layer this is the

@@ -185,6 +185,116 @@ def run_serve(args, kvc):
     print(json.dumps(result), flush=True)
 
 
+BASELINES_DESC = ("GQA decode batch (256 sequences, 32/8 heads, head_dim 128, context lognormal "
+                  "median 1024, clip [16, 8192], block 16) run ragged and paged, against the "
+                  "same rows left-padded to the longest context, and the cache footprint of a "
+                  "contiguous max-length (8192) cache")
+
+
+def time_decode_batch(kvc, ctx, hq, hkv, a, bs, steps, warmup, seed=0, reserve_len=None):
+    """Microseconds per call of one decode batch (one new token per sequence at
+    the given contexts) on random GPU-drawn data.  Paged: each sequence holds
+    just the blocks it needs, in shuffled pool order.  reserve_len set: a
+    contiguous cache that reserves reserve_len slots per sequence (sequence i
+    owns the consecutive blocks i*R .. i*R+R-1, R = reserve_len / block)."""
+    s = len(ctx)
+    nblk = [-(-(int(c) + 1) // bs) for c in ctx]
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    if reserve_len is None:
+        nb, mb = sum(nblk), max(nblk)
+        perm = torch.randperm(nb, generator=g, device="cuda").to(torch.int32).cpu().numpy()
+        table = np.full((s, mb), -1, np.int32)
+        o = 0
+        for i, n in enumerate(nblk):
+            table[i, :n] = perm[o:o + n]
+            o += n
+    else:
+        mb = -(-int(reserve_len) // bs)
+        assert max(nblk) <= mb
+        nb = s * mb
+        table = (np.arange(s, dtype=np.int64)[:, None] * mb + np.arange(mb)[None, :]).astype(np.int32)
+    kc = torch.randn(nb, hkv, bs, a, generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn(nb, hkv, bs, a, generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn(s, hq, a, generator=g, device="cuda").to(torch.bfloat16)
+    kn = torch.randn(s, hkv, a, generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(s, hkv, a, generator=g, device="cuda").to(torch.bfloat16)
+    cu = dev_i32(np.arange(s + 1))
+    cx = dev_i32(np.asarray(ctx))
+    tb = dev_i32(table)
+    mc = int(max(ctx))
+    ws = kvc.new_workspace(s, s, 1, mc, hq, hkv, a, bs)
+    out = torch.empty_like(q)
+    call = lambda: kvc.kvc_paged_attention_varlen(  # noqa: E731
+        out, q, kn, vn, kc, vc, tb, cu, cx, 1.0 / math.sqrt(a), max_q_len=1, max_context_len=mc,
+        workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    assert kvc.kvc_workspace_flags(ws) == 0
+    del kc, vc
+    return us
+
+
+def run_baselines(args, kvc):
+    """The decode batch ragged and paged vs left-padded; paged vs contiguous
+    max-length cache footprint (helpers in batching_kv_append_amd.baselines)."""
+    from batching_kv_append_amd import baselines as base
+    torch.cuda.set_device(0)
+    hq, hkv, a, bs, max_len = 32, 8, 128, 16, 8192
+    rng = np.random.default_rng(2 if args.seed is None else args.seed)
+    ctx = np.clip(np.rint(np.exp(rng.normal(math.log(1024.0), 0.8, size=256))), 16, max_len)
+    ctx = [int(c) for c in ctx]
+    lens = [c + 1 for c in ctx]  # cached tokens after the step's append
+    ragged_us = time_decode_batch(kvc, ctx, hq, hkv, a, bs, args.steps, args.warmup)
+    padded_us = time_decode_batch(kvc, [max(ctx)] * len(ctx), hq, hkv, a, bs, args.steps,
+                                  args.warmup)
+    contiguous_us = time_decode_batch(kvc, ctx, hq, hkv, a, bs, args.steps, args.warmup,
+                                      reserve_len=max_len + 1)
+    useful, pads = base.left_padded_tokens(lens)
+    paged = base.paged_cache_bytes(lens, bs, hkv, a)
+    contiguous = base.contiguous_cache_bytes(len(lens), max_len, hkv, a)  # as the pages size it
+    # how many such sequences fit in 64 GiB of cache, drawn from the same law
+    lens_many = np.clip(np.rint(np.exp(rng.normal(math.log(1024.0), 0.8, size=200000))), 16,
+                        max_len).astype(np.int64) + 1
+    budget = 64 << 30
+    per_token = 2 * hkv * a * 2
+    fit_paged = base.sequences_that_fit(budget, (-(-int(x) // bs) * bs * per_token for x in lens_many))
+    fit_contig = base.sequences_that_fit(budget, (max_len * per_token for _ in lens_many))
+    kv_bytes = sum(lens) * per_token
+    result = {
+        "metric": METRIC, "value": len(ctx) / (ragged_us * 1e-6), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ragged_us / 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded lengths; GPU-drawn random K/V and rows)",
+        "config": {"workload": BASELINES_DESC, "name": "baselines", "num_seqs": len(ctx),
+                   "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": a, "block_size": bs},
+        "roofline": {"bound": "hbm", "kernel": "decode step (prep + decode + merge)",
+                     "achieved": kv_bytes / (ragged_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": kv_bytes / (ragged_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": kv_bytes,
+                     "avg_launch_us": ragged_us},
+        "baselines": {
+            "ragged_paged_us": ragged_us, "left_padded_us": padded_us,
+            "padded_over_ragged_time": padded_us / ragged_us,
+            "contiguous_max_len_cache_us": contiguous_us,
+            "contiguous_over_paged_time": contiguous_us / ragged_us,
+            "useful_cached_tokens": useful, "pad_tokens": pads,
+            "pad_fraction_of_padded_batch": pads / (useful + pads),
+            "paged_cache_bytes": paged, "contiguous_max_len_cache_bytes": contiguous,
+            "contiguous_waste_fraction": 1 - kv_bytes / contiguous,
+            "paged_waste_fraction": 1 - kv_bytes / paged,
+            "sequences_in_64GiB_paged": fit_paged, "sequences_in_64GiB_contiguous": fit_contig,
+            "insert_prompt_padding_B8_n100": base.insert_padding_tokens(8, 100),
+        },
+    }
+    print(json.dumps(result), flush=True)
+
+
 def dev_bits(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -347,7 +457,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS) + ["serve"],
+    ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS) + ["serve", "baselines"],
                     help="serve: scheduler-driven steps over a request trace (use e.g. "
                          "--steps 300 --warmup 300)")
     ap.add_argument("--seed", type=int, default=None)
@@ -379,6 +489,9 @@ def main():
 
     if args.workload == "serve":
         run_serve(args, kvc)
+        return
+    if args.workload == "baselines":
+        run_baselines(args, kvc)
         return
     desc, make = WORKLOADS[args.workload]
     t0 = time.perf_counter()

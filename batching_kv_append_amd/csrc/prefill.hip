@@ -25,14 +25,17 @@
 // blocks of QW = 32 positions; each wave owns one (head, 32 positions).  K/V
 // tiles of 64 keys (gathered block by block through the block table) are
 // staged in LDS, double-buffered, once per workgroup and shared by the HPW
-// heads of the group (GQA, e2hang/Notes "MQA与GQA").  K is stored row-major
-// with a 16-byte XOR swizzle; V is stored transposed ([dim][key], keys
-// permuted so a lane's eight P.V keys are one 16-byte chunk) with a 16-byte
-// XOR swizzle, so both operand reads are single conflict-free ds_read_b128.
-// Each loading thread owns 4 consecutive keys x 8 dims: its V^T stores are
-// eight 8-byte writes.  The planning kernel lists the
-// workgroups costliest first.
+// heads of the group (GQA, e2hang/Notes "MQA与GQA").  K and V are both stored
+// row-major, as they sit in the cache, each with its own 16-byte XOR swizzle:
+// the K operand is one ds_read_b128 per lane, and the V^T operand is read
+// with the transposing LDS load of gfx950 (ds_read_b64_tr_b16: within each
+// 16-lane group, lane o receives element o % 4 of the 8-byte loads of lanes
+// 4j + o / 4, j = 0..3), two per MFMA, so no transpose is done by the ALUs.
+// Each loading thread owns 4 consecutive keys x 8 dims and writes them with
+// 16-byte stores.  The planning kernel lists the workgroups costliest first.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kvc_launch.h"
 
@@ -43,6 +46,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
 struct PrefillParams {
     const uint16_t* q;
@@ -87,15 +92,6 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Low / high 16-bit halves of two words, packed: (a.lo | b.lo << 16), (a.hi | b.hi << 16).
-// One v_perm_b32 each: bytes 0-3 of the selector space are `a`, 4-7 are `b`.
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
 // acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 with (1, 1)).
 __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -103,10 +99,39 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
 }
 
-// XOR swizzle of the 16-byte chunks of V^T row d.  Reads: 8 (or 16)
-// consecutive rows d at one logical chunk hit distinct bank groups.  Writes:
-// rows d = 8*cc + e of one e over cc = 0..7 hit distinct chunks.
-__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+// XOR swizzle of the 16-byte chunks of V row `row` (a key of the tile):
+// 0, 6, 10, 12 for row % 4 = 0..3, and 8 more when row % 16 >= 8.  A
+// transposing read takes 4 consecutive rows x 2 (16 lanes) or 4 (32 lanes)
+// consecutive chunks; bits 1-2 and bits 2-3 of the four swizzles are both
+// all distinct, so either lane group hits distinct banks.  16-byte row
+// writes by the tile loaders (8 chunks of rows k and k + 8 per 16 lanes) are
+// conflict-free as well.
+template <int CPR>
+__device__ __forceinline__ int vswz(int row) {
+    return (((row & 1) * 6) ^ (((row >> 1) & 1) * 10) ^ (row & 8)) & (CPR - 1);
+}
+
+// Combine x of lanes l and l ^ 32 with the gfx950 half-wave swap
+// (v_permlane32_swap trades one half-wave of its first operand with the other
+// half-wave of its second), in the VALU rather than through the LDS crossbar.
+// Swapping x with itself leaves every lane holding its own value in one
+// result and its partner's in the other, so max and sum of the pair are the
+// same whichever result is which.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 8-byte transposing LDS read (ds_read_b64_tr_b16) at a byte address of a
+// __shared__ array.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)const_cast<char*>(p));
+}
 
 template <int A, int BS, int HPW>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
@@ -122,8 +147,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
     static_assert(LOADERS <= 256, "tile loaders");
     static_assert(BS % 4 == 0, "4 consecutive keys must share a block");
 
-    __shared__ uint4 sK[2][TK * CPR];       // [key][chunk ^ (key % CPR)]
-    __shared__ uint4 sVt[2][A * (TK / 8)];  // [dim][8-key chunk ^ vswz(dim)]
+    __shared__ uint4 sK[2][TK * CPR];  // [key][chunk ^ (key % CPR)]
+    __shared__ uint4 sV[2][TK * CPR];  // [key][chunk ^ vswz(key)]
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -169,18 +194,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m = NEG_BIG;  // running maximum, scaled log2 units
-    float lsum = 0.f;
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // partial denominators, one per 16-key step
 
     // ---- cooperative tile loads: thread = 4 consecutive keys x one chunk ----
-    // Keys at or past L load a copy of row L-1 (same 4-aligned group, so the
-    // same block): their weight is exactly 0 for every row that is stored,
-    // and the copy keeps their values finite.
+    // The 4 keys of a group share one cache block (k0 and 4 kg are multiples
+    // of 4, and so is the block size), so a thread reads 4 rows of one block
+    // at fixed offsets.  A group at or past L reads the rows of the block
+    // that holds key L-1 instead (memory of that block, whatever it holds):
+    // keys >= L are masked out of every stored row's scores by select, and
+    // their V rows are zeroed before they reach LDS, so their weight of 0
+    // never meets a non-finite value.
     const bool loader = tid < LOADERS;
     // Thread -> (key group kg: keys 4kg .. 4kg+3, 16-byte chunk cc: dims
     // 8cc .. 8cc+7).  Wave w covers key groups 4w .. 4w+3.  For A = 128 each
     // 16-lane group holds chunks 8h .. 8h+7 of key groups kg and kg ^ 2, so
-    // its eight-byte V^T stores land on 16 distinct bank pairs (kg and kg ^ 2
-    // write opposite halves of a 16-byte unit).
+    // its 16-byte stores (one row per store) hit 16 distinct bank groups.
     int kg, cc;
     if constexpr (CPR == 16) {
         kg = ((tid >> 5) & 1) | (((tid >> 3) & 1) << 1) | ((tid >> 6) << 2);
@@ -189,10 +217,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
         kg = tid / CPR;
         cc = tid % CPR;
     }
-    // V^T key order: key 16a+8b+4c+e is stored at 16a+8c+4b+e, so the eight
-    // keys a lane feeds to one P.V step (16a+4c+{0..3} and 16a+8+4c+{0..3})
-    // form one 16-byte chunk (2a+c) of the transposed row.
-    const int vunit = 4 * (kg >> 2) + 2 * (kg & 1) + ((kg >> 1) & 1);
+    // offset (16-byte units) of the thread's first row inside a cache block
+    const uint32_t toff = (uint32_t)((kvh * BS + (4 * kg) % BS) * CPR + cc);
+    const uint32_t blk_stride = (uint32_t)(P.hkv * BS * CPR);
     u32x4_t kreg[4], vreg[4];  // native vectors: the staging stays in VGPRs
     int bad = 0;
     // Block-table entry of this thread's key group in the tile at k0 (-1 past
@@ -205,63 +232,60 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
         short_tbl = 1;
         return 0;  // in range; the result is flagged
     };
-    auto load_tile = [&](int k0, int entry) __attribute__((always_inline)) {
+    auto load_tile = [&](int entry) __attribute__((always_inline)) {
         if (!loader) return;
-        const int key0 = min(k0 + 4 * kg, L - 1);  // the (clamped) 4 keys share one block
-        int64_t blk = entry;
-        if (blk < 0 || blk >= P.num_blocks) {
+        uint32_t blk = (uint32_t)entry;
+        if (entry < 0 || (int64_t)entry >= P.num_blocks) {
             bad = 1;
             blk = 0;
         }
-        const int64_t base = ((blk * P.hkv + kvh) * BS + key0 % BS) * CPR + cc;
+        const uint64_t base = (uint64_t)blk * blk_stride + toff;
         const uint4* kp = P.k_cache + base;
         const uint4* vp = P.v_cache + base;
-        if (k0 + 4 * kg + 3 < L) {  // whole group in range: constant row offsets
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kreg[j] = __builtin_bit_cast(u32x4_t, kp[j * CPR]);
-                vreg[j] = __builtin_bit_cast(u32x4_t, vp[j * CPR]);
-            }
-        } else {  // the sequence's last keys: rows past L repeat row L-1
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int dj = min(k0 + 4 * kg + j, L - 1) - key0;
-                kreg[j] = __builtin_bit_cast(u32x4_t, kp[dj * CPR]);
-                vreg[j] = __builtin_bit_cast(u32x4_t, vp[dj * CPR]);
-            }
+        for (int j = 0; j < 4; ++j) {
+            kreg[j] = __builtin_bit_cast(u32x4_t, kp[j * CPR]);
+            vreg[j] = __builtin_bit_cast(u32x4_t, vp[j * CPR]);
         }
     };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    auto store_tile = [&](int buf, int k0) __attribute__((always_inline)) {
         if (!loader) return;
+        if (k0 + 4 * kg + 3 >= L) {  // the sequence's last keys: V rows past L are zero
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (k0 + 4 * kg + j >= L) vreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = 4 * kg + j;
             sK[buf][key * CPR + (cc ^ (key % CPR))] = __builtin_bit_cast(uint4, kreg[j]);
-        }
-        const u32x4_t w0 = vreg[0], w1 = vreg[1], w2 = vreg[2], w3 = vreg[3];
-        uint2* vt = reinterpret_cast<uint2*>(&sVt[buf][0]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = cc * 8 + e;
-            const int w = e >> 1;
-            uint2 v;
-            if (e & 1) {
-                v.x = pack_hi(w0[w], w1[w]);
-                v.y = pack_hi(w2[w], w3[w]);
-            } else {
-                v.x = pack_lo(w0[w], w1[w]);
-                v.y = pack_lo(w2[w], w3[w]);
-            }
-            const int chunk = (vunit >> 1) ^ vswz(d);
-            vt[(d * (TK / 8) + chunk) * 2 + (vunit & 1)] = v;
+            sV[buf][key * CPR + (cc ^ vswz<CPR>(key))] = __builtin_bit_cast(uint4, vreg[j]);
         }
     };
+    // Transposing-read offsets (bytes inside a V tile) of this lane for the
+    // V^T operand of output tile dt, keys 8 rd + {0..3} of a 16-key step: the
+    // lane is source 4j + q of its 16-lane group g, so it points at key row
+    // 4 (g / 2) + j + 8 rd, dims 32 dt + 16 (g % 2) + 4q .. +3.  Rows of the
+    // other steps are 16 or 32 keys further, which keeps the swizzle, so they
+    // are constant offsets.  With A = 16 the lanes of dims 16..31 read chunk 0
+    // and their operand is replaced by zeros.
+    int troff[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int g = lane >> 4, q = lane & 3, j = (lane >> 2) & 3;
+            const int row = 4 * (g >> 1) + j + 8 * rd;
+            int chunk = dt * 4 + 2 * (g & 1) + (q >> 1);
+            if (chunk >= CPR) chunk = 0;
+            troff[dt][rd] = row * CPR * 16 + (chunk ^ vswz<CPR>(row)) * 16 + (q & 1) * 8;
+        }
 
     int entry_next = 0;  // table entry of the tile after the one being loaded
     if (nkt > 0) {
-        load_tile(0, table_entry(0));
+        load_tile(table_entry(0));
         if (nkt > 1) entry_next = table_entry(TK);
-        store_tile(0);
+        store_tile(0, 0);
     }
     __syncthreads();
     // Explicit wait for everything issued so far (the Q^T operand loads are
@@ -269,13 +293,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
     // flight inside the loop and waits for ALL loads, the next tile's
     // included, before the first MFMA of every tile).
     __builtin_amdgcn_s_waitcnt(0);
-    for (int t = 0; t < nkt; ++t) {
+    // One tile step; the buffer index is a compile-time constant (the loop
+    // below is unrolled by two), so every LDS address of a step is a per-lane
+    // register plus an immediate.
+    auto tile_step = [&](const int t, auto bufc) __attribute__((always_inline)) {
+        constexpr int buf = decltype(bufc)::value;
         const int k0 = t * TK;
-        const int buf = t & 1;
         if (t + 1 < nkt) {  // in flight during this tile's math
             const int entry = entry_next;
             if (t + 2 < nkt) entry_next = table_entry(k0 + 2 * TK);
-            load_tile(k0 + TK, entry);
+            load_tile(entry);
         }
 
         if (k0 < kend_w) {
@@ -320,19 +347,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
                         if (key > lim) sacc[kh][r] = -INFINITY;
                     }
             }
-            float mx = -INFINITY;
+            // column maximum: four independent chains, then the other half-wave
+            float mq[4];
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int i = 0; i < 4; ++i) {
+                mq[i] = fmaxf(sacc[i >> 1][(i & 1) * 8], sacc[i >> 1][(i & 1) * 8 + 1]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kh][r]);
-            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+                for (int r = 2; r < 8; ++r) mq[i] = fmaxf(mq[i], sacc[i >> 1][(i & 1) * 8 + r]);
+            }
+            float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+            mx = halves_max(mx);
             const float cand = pos_scale ? mx * cs : mx;  // column max, scaled log2 units
             const bool grow = cand > m + RESCALE_SLACK;
             if (__any(grow)) {
                 const float m_new = grow ? cand : m;
                 const float alpha = __builtin_amdgcn_exp2f(m - m_new);
                 m = m_new;
-                lsum *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -353,40 +385,51 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
                     pb[kh][ks].w = pack_bf16x2(p[ks * 8 + 6], p[ks * 8 + 7]);
                     // the denominator sums the same bf16 weights the P.V
                     // product uses: one dot2 with (1, 1) per pair
-                    lsum = sum_bf16x2(pb[kh][ks].x, lsum);
-                    lsum = sum_bf16x2(pb[kh][ks].y, lsum);
-                    lsum = sum_bf16x2(pb[kh][ks].z, lsum);
-                    lsum = sum_bf16x2(pb[kh][ks].w, lsum);
+                    float& ls = lsum[kh * 2 + ks];
+                    ls = sum_bf16x2(pb[kh][ks].x, ls);
+                    ls = sum_bf16x2(pb[kh][ks].y, ls);
+                    ls = sum_bf16x2(pb[kh][ks].z, ls);
+                    ls = sum_bf16x2(pb[kh][ks].w, ls);
                 }
             }
 
             __builtin_amdgcn_s_setprio(2);
             // ---- O^T += V^T P^T ---------------------------------------------
+            // Operand slot e of lane l holds V[key][32 dt + l % 32] for key
+            // 32 kh + 16 ks + 8 (e / 4) + 4 (l / 32) + e % 4, the key order of
+            // the P^T slots.
+            const char* vb = reinterpret_cast<const char*>(&sV[buf][0]);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 32 + col;
-                const int sw = vswz(d);
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
-                        uint4 a = make_uint4(0, 0, 0, 0);
-                        if (d < A) a = sVt[buf][d * (TK / 8) + ((2 * (2 * kh + ks) + hi) ^ sw)];
-                        o[dt] = mfma32(a, pb[kh][ks], o[dt]);
+                        const int rb = (kh * 32 + ks * 16) * CPR * 16;
+                        const i16x4_t v0 = lds_read_tr16(vb + troff[dt][0] + rb);
+                        const i16x4_t v1 = lds_read_tr16(vb + troff[dt][1] + rb);
+                        i16x8_t a8 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        if (A < 32 && (lane & 16)) a8 = i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                        o[dt] = mfma32(__builtin_bit_cast(uint4, a8), pb[kh][ks], o[dt]);
                     }
             }
         }
 
         __builtin_amdgcn_s_setprio(0);
-        if (t + 1 < nkt) store_tile(buf ^ 1);
+        if (t + 1 < nkt) store_tile(buf ^ 1, k0 + TK);
         __syncthreads();
+    };
+    for (int t = 0; t < nkt; t += 2) {
+        tile_step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < nkt) tile_step(t + 1, std::integral_constant<int, 1>{});
     }
     if (short_tbl) atomicOr(P.hdr + HDR_FLAGS, FLAG_TABLE_SHORT);
     if (bad) atomicOr(P.hdr + HDR_FLAGS, FLAG_BAD_BLOCK);
 
     // ---- normalise and store ------------------------------------------------
     const int pos = p0 + col;
-    const float lt = lsum + shfl_xor_f(lsum, 32);
+    const float lw = (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    const float lt = halves_sum(lw);
     if (pos < qlen) {
         const float inv = 1.f / lt;
         uint16_t* orow = P.out + ((int64_t)(row0 + pos) * P.hq + h) * A;

@@ -121,7 +121,7 @@ struct Profiler {
     bool on = false;
     int32_t max_calls = 0, calls = 0;
     std::vector<hipEvent_t> ev;  // 2 * KVC_PROF_PHASES per call: (start, end) per phase
-    std::vector<uint8_t> used;   // per call and phase: both events recorded
+    std::vector<uint8_t> used;   // per call and phase: 1 both events recorded, 2 a record failed
 };
 Profiler g_prof;
 std::mutex g_prof_mu;
@@ -129,8 +129,10 @@ std::mutex g_prof_mu;
 void prof_mark(int phase, bool end, hipStream_t st) {
     if (!g_prof.on || g_prof.calls >= g_prof.max_calls) return;
     const size_t base = (size_t)g_prof.calls * KVC_PROF_PHASES + phase;
-    hipEventRecord(g_prof.ev[base * 2 + (end ? 1 : 0)], st);
-    if (end) g_prof.used[base] = 1;
+    if (hipEventRecord(g_prof.ev[base * 2 + (end ? 1 : 0)], st) != hipSuccess)
+        g_prof.used[base] = 2;  // a phase with a failed record is left out of the sums
+    else if (end && g_prof.used[base] == 0)
+        g_prof.used[base] = 1;
 }
 
 // Side stream per device for the prefill kernel, so the matrix-bound prefill
@@ -173,7 +175,7 @@ extern "C" int kvc_profile_begin(int32_t max_calls) {
     if (max_calls < 1 || max_calls > 100000)
         return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_profile_begin: max_calls out of range");
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
     g_prof = Profiler{};
     g_prof.ev.resize((size_t)max_calls * KVC_PROF_PHASES * 2);
     g_prof.used.assign((size_t)max_calls * KVC_PROF_PHASES, 0);
@@ -194,7 +196,7 @@ extern "C" int kvc_profile_end(double* ms_sum, int32_t* calls) {
     for (int32_t c = 0; c < g_prof.calls; ++c) {
         for (int p = 0; p < KVC_PROF_PHASES; ++p) {
             const size_t base = (size_t)c * KVC_PROF_PHASES + p;
-            if (!g_prof.used[base]) continue;
+            if (g_prof.used[base] != 1) continue;
             hipError_t r = hipEventSynchronize(g_prof.ev[base * 2 + 1]);
             float ms = 0.f;
             if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_prof.ev[base * 2], g_prof.ev[base * 2 + 1]);
@@ -203,7 +205,7 @@ extern "C" int kvc_profile_end(double* ms_sum, int32_t* calls) {
         }
     }
     *calls = g_prof.calls;
-    for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
     g_prof = Profiler{};
     return KVC_OK;
 }

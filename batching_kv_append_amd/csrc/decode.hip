@@ -446,13 +446,6 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);  // a.lo | b.lo << 16
-}
-__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.hi | b.hi << 16
-}
-
 // NG: 16-column groups of q heads per wave (1, or 2 for 32 heads on one kv
 // head, as in MQA): the groups share every K fragment and the V^T tile, so
 // the partition's K/V is read once for all of them.

@@ -184,7 +184,9 @@ int kvc_scheduler_create(kvc_allocator* alloc, int32_t token_budget, int32_t max
 /* Destroy; blocks still held by running requests return to the allocator. */
 void kvc_scheduler_destroy(kvc_scheduler* s);
 /* Queue a request.  prompt_len, max_new_tokens >= 1; KVC_ERR_INVALID_ARG if
- * it could never fit a table row or the pool. */
+ * it could never fit a table row or the pool.  request_id is the caller's tag,
+ * handed back by step and complete; requests are tracked by admission order,
+ * so ids need not be unique. */
 int kvc_scheduler_add(kvc_scheduler* s, int64_t request_id, int32_t prompt_len,
                       int32_t max_new_tokens);
 /* Plan the next step into host arrays with capacity max_seqs (+1 for

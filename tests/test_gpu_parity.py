@@ -2,7 +2,7 @@
 
 Bar: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3 over the
 compared rows, bf16 inputs and bf16 output.  The small cases span several
-tiles, partitions and ragged tails; the five workloads run at full size
+tiles, partitions and ragged tails; the six workloads run at full size
 (every row for the decode and mixed steps; sampled rows, computed one by one
 by the oracle, for the 32K-token prompt and the shared-prefix step)."""
 import math
@@ -91,7 +91,7 @@ def test_toy_chunked_then_decode(kvc, orc):
         compare(g[2 + t - 7], ru[t:t + 1], what=f"toy decode {t}")
 
 
-@pytest.mark.parametrize("cfg", ["decode_mha", "decode_gqa", "mixed"])
+@pytest.mark.parametrize("cfg", ["decode_mha", "decode_gqa", "decode_mqa", "mixed"])
 def test_full_workload(kvc, orc, cfg):
     wl = getattr(W, cfg)()
     (g,), _, _ = run_steps(kvc, wl)

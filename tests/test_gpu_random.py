@@ -1,0 +1,63 @@
+"""Seeded random shapes against the oracle: many small ragged batches that mix
+decode rows, prompt chunks and empty rows, over the supported head groupings
+(G = 1, 2 or a multiple of 4), block sizes 4 and 16 and head dims 16 and 128,
+with context lengths drawn around block, tile and partition boundaries.  Same
+bar as the other parity tests (max |diff| <= 2e-2, mean <= 2e-3); the pools
+after the call equal the oracle's bit for bit."""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import compare, host_bits, oracle_run, run_steps
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+# context lengths near the edges the kernels care about: blocks (4, 16),
+# prefill key tiles (64), decode partitions (256)
+EDGES = [0, 1, 3, 4, 5, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513]
+
+
+def _case(i):
+    rng = np.random.default_rng(1000 + i)
+    g = int(rng.choice([1, 2, 4, 8, 12, 16, 32, 64]))
+    hkv = int(rng.choice([1, 2, 3])) if g <= 16 else 1
+    a = 16 if rng.random() < 0.25 else 128
+    bs = int(rng.choice([4, 16]))
+    n = int(rng.integers(1, 13))
+    specs = []
+    for _ in range(n):
+        c = int(rng.choice(EDGES)) if rng.random() < 0.5 else int(rng.integers(0, 1500))
+        r = rng.random()
+        if r < 0.45:
+            q = 1                          # decode row
+        elif r < 0.55:
+            q = 0                          # sequence with no new rows
+        else:
+            q = int(rng.integers(2, 131))  # prompt chunk
+        specs.append((c, q))
+    if sum(q for _, q in specs) == 0:
+        specs[0] = (specs[0][0], 1)
+    return dict(name=f"rand{i:02d}_g{g}_hkv{hkv}_a{a}_bs{bs}", specs=specs, hq=g * hkv,
+                hkv=hkv, a=a, bs=bs, seed=2000 + i)
+
+
+CASES = [_case(i) for i in range(N_CASES)]
+
+
+@pytest.fixture(scope="module")
+def kvc():
+    import batching_kv_append_amd as m
+    return m
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_random_shapes(kvc, orc, case):
+    wl = W.make_step_workload(case["name"], case["specs"], num_q_heads=case["hq"],
+                              num_kv_heads=case["hkv"], head_dim=case["a"],
+                              block_size=case["bs"], seed=case["seed"])
+    (g,), kc, vc = run_steps(kvc, wl)
+    (r,), kp, vp = oracle_run(orc, wl)
+    compare(g, r, what=case["name"])
+    # the append is a bit copy: both pools equal the oracle's, untouched slots included
+    assert np.array_equal(host_bits(kc), kp) and np.array_equal(host_bits(vc), vp)

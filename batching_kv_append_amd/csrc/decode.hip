@@ -43,12 +43,13 @@ struct PrepParams {
     const int32_t* cu;
     const int32_t* ctx;
     int32_t num_seqs, total_q, max_q_len, max_context_len, span;
+    int32_t gp;  // decode partitions per work item
     int64_t cap_dec, cap_pre;
     int32_t* hdr;
     int2* dec_items;
     int2* pre_items;
     int2* pre_sorted;
-    int4* merge_list;  // (sequence, first item, partitions, output row)
+    int4* merge_list;  // (sequence, first item, items, output row)
     // append (k_new == nullptr: nothing to append)
     const uint4* k_new;
     const uint4* v_new;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     const int32_t* __restrict__ cu = P.cu;
     const int32_t* __restrict__ ctx = P.ctx;
     const int32_t num_seqs = P.num_seqs, total_q = P.total_q, max_q_len = P.max_q_len;
-    const int32_t max_context_len = P.max_context_len, span = P.span;
+    const int32_t max_context_len = P.max_context_len, span = P.span, gp = P.gp;
     const int64_t cap_dec = P.cap_dec, cap_pre = P.cap_pre;
     int32_t* hdr = P.hdr;
     int2* dec_items = P.dec_items;
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
                 q = 0;
             }
             if (q == 1) {
-                nd = (c + 1 + DECODE_PART - 1) / DECODE_PART;
+                const int parts = (c + 1 + DECODE_PART - 1) / DECODE_PART;
+                nd = (parts + gp - 1) / gp;  // work items of gp partitions
                 nm = nd > 1;
             } else if (q >= 2) {
                 np = (q + span - 1) / span;
@@ -449,7 +451,13 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // NG: 16-column groups of q heads per wave (1, or 2 for 32 heads on one kv
 // head, as in MQA): the groups share every K fragment and the V^T tile, so
 // the partition's K/V is read once for all of them.
-template <int BS, int NG>
+// GP: partitions per work item.  GP = 1: each wave is one (partition, kv
+// head, head chunk).  GP = 4 (NG = 1): a workgroup is one (group of four
+// consecutive partitions, kv head, head chunk); wave w takes partition
+// 4 x group + w, and the last of the group's waves to finish combines their
+// four (max, sum, accumulator) in LDS, in wave order, into the output (a
+// sequence of at most four partitions) or into one partial per group.
+template <int BS, int NG, int GP>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     constexpr int A = 128;
     constexpr int CPR = A / 8;              // 16-byte chunks per row
@@ -459,16 +467,25 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     static_assert(NT <= 64, "table slice must fit one VGPR");
     static_assert(BS % 4 == 0, "4 consecutive tokens must share a block");
 
-    // per wave: V^T of one 32-token step, [dim][4 chunks of 8 tokens], 64 B rows
+    static_assert(GP == 1 || (GP == 4 && NG == 1), "partition groups need one column group");
+
+    // per wave: V^T of one 32-token step, [dim][4 chunks of 8 tokens], 64 B
+    // rows; with GP = 4 it then holds the wave's accumulator for the combine
     __shared__ uint4 sVt[4][A * 4];
+    __shared__ float sML[GP > 1 ? 4 : 1][2][16];  // per wave: column max, column total
+    __shared__ int arrived;                        // waves of the group done
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int col = lane & 15;  // head column
     const int g = lane >> 4;    // token group: tokens 4g..4g+3 of each 16-token block
     const int64_t n_units = (int64_t)P.hdr[HDR_N_DEC] * P.hkv * P.HC;
-    const int64_t u = (int64_t)blockIdx.x * 4 + wave;
-    if (u >= n_units) return;
+    const int64_t u = GP > 1 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + wave;
+    if (u >= n_units) return;  // GP > 1: the whole workgroup
+    if constexpr (GP > 1) {
+        if (threadIdx.x == 0) arrived = 0;
+        __syncthreads();  // the only barrier: waves past the sequence leave below
+    }
     uint4* vt = &sVt[wave][0];
 
     const int GW = P.G / P.HC;  // heads of this wave (<= 16 * NG)
@@ -476,10 +493,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     const int kvh = (u / P.HC) % P.hkv;
     const int item = u / (P.HC * P.hkv);
     const int2 it = P.items[item];
-    const int s = it.x, part = it.y;
+    const int s = it.x;
     const int L = P.ctx[s] + 1;
     const int row = P.cu[s];
     const int nparts = (L + DECODE_PART - 1) / DECODE_PART;
+    const int part = GP > 1 ? it.y * GP + wave : it.y;
+    if (part >= nparts) return;  // GP > 1: the group runs past the sequence
+    const int nact = min(GP, nparts - it.y * GP);  // waves of this group with work
+    const int ngroups = (nparts + GP - 1) / GP;    // work items of the sequence
     const int t0 = part * DECODE_PART;
     const int t1 = min(L, t0 + DECODE_PART);
     const int h0 = kvh * P.G + hc * GW;
@@ -667,34 +688,88 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     }
 
     // ---- column totals and output ----------------------------------------------
+    float lt[NG];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
-        float lt = lsum[ng] + __shfl_xor(lsum[ng], 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
-        if (16 * ng + col < GW) {
-            const int h = h0 + 16 * ng + col;
-            if (nparts == 1) {
-                const float inv = 1.f / lt;
-                uint16_t* orow = P.out + ((int64_t)row * P.hq + h) * A;
+        lt[ng] = lsum[ng] + __shfl_xor(lsum[ng], 16, 64);
+        lt[ng] += __shfl_xor(lt[ng], 32, 64);
+    }
+    // normalised bf16 output of column group ng (scaled by inv)
+    auto write_out = [&](int ng, const f32x4_t (&acc)[8], float inv) {
+        uint16_t* orow = P.out + ((int64_t)row * P.hq + h0 + 16 * ng + col) * A;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) {
-                    uint2 v;
-                    v.x = pack_bf16x2(o[ng][dt][0] * inv, o[ng][dt][1] * inv);
-                    v.y = pack_bf16x2(o[ng][dt][2] * inv, o[ng][dt][3] * inv);
-                    *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * g) = v;
-                }
-            } else {
-                const int64_t slot = (int64_t)item * P.hq + h;
-                float* acc = P.ws_acc + slot * A;
+        for (int dt = 0; dt < 8; ++dt) {
+            uint2 v;
+            v.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+            v.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+            *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * g) = v;
+        }
+    };
+    // split-K partial (max, total, fp32 accumulator) of work item `item`
+    auto write_partial = [&](int ng, const f32x4_t (&acc)[8], float mm, float ll) {
+        const int64_t slot = (int64_t)item * P.hq + h0 + 16 * ng + col;
+        float* dst = P.ws_acc + slot * A;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-                    *reinterpret_cast<float4*>(acc + dt * 16 + 4 * g) =
-                        make_float4(o[ng][dt][0], o[ng][dt][1], o[ng][dt][2], o[ng][dt][3]);
-                if (g == 0) {
-                    P.ws_ml[slot * 2] = m[ng];
-                    P.ws_ml[slot * 2 + 1] = lt;
-                }
+        for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<float4*>(dst + dt * 16 + 4 * g) =
+                make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+        if (g == 0) {
+            P.ws_ml[slot * 2] = mm;
+            P.ws_ml[slot * 2 + 1] = ll;
+        }
+    };
+    if (nparts == 1) {
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng)
+            if (16 * ng + col < GW) write_out(ng, o[ng], 1.f / lt[ng]);
+        return;
+    }
+    if constexpr (GP == 1) {
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng)
+            if (16 * ng + col < GW) write_partial(ng, o[ng], m[ng], lt[ng]);
+    } else {
+        // Combine the group in LDS.  Each wave leaves its column max and
+        // total and its accumulator (in its own V^T tile, no longer read),
+        // then counts itself in; the wave that arrives last combines the
+        // group in wave order (fixed, so the result does not depend on which
+        // wave that is).
+        float4* mine = reinterpret_cast<float4*>(vt);
+        if (g == 0) {
+            sML[wave][0][col] = m[0];
+            sML[wave][1][col] = lt[0];
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            mine[dt * 64 + lane] = make_float4(o[0][dt][0], o[0][dt][1], o[0][dt][2], o[0][dt][3]);
+        __threadfence_block();  // this wave's LDS writes before its arrival
+        int before = 0;
+        if (lane == 0) before = atomicAdd(&arrived, 1);
+        before = __shfl(before, 0, 64);
+        if (before != nact - 1) return;
+        __threadfence_block();  // every other wave's writes after the last arrival
+        float mm = -INFINITY;
+        for (int w = 0; w < nact; ++w) mm = fmaxf(mm, sML[w][0][col]);
+        float ll = 0.f;
+        f32x4_t acc[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < nact; ++w) {
+            const float sc = __builtin_amdgcn_exp2f(sML[w][0][col] - mm);
+            ll += sc * sML[w][1][col];
+            const float4* src = reinterpret_cast<const float4*>(&sVt[w][0]);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const float4 v = src[dt * 64 + lane];
+                acc[dt][0] += sc * v.x;
+                acc[dt][1] += sc * v.y;
+                acc[dt][2] += sc * v.z;
+                acc[dt][3] += sc * v.w;
             }
+        }
+        if (col < GW) {
+            if (ngroups == 1) write_out(0, acc, 1.f / ll);
+            else write_partial(0, acc, mm, ll);
         }
     }
 }
@@ -834,6 +909,7 @@ hipError_t launch_prep(const StepArgs& a, bool with_append) {
     p.max_q_len = a.max_q_len;
     p.max_context_len = a.max_context_len;
     p.span = prefill_span(G);
+    p.gp = decode_group_parts(G, a.head_dim);
     p.cap_dec = a.lay.cap_dec;
     p.cap_pre = a.lay.cap_pre;
     p.hdr = (int32_t*)(ws + a.lay.hdr);
@@ -880,20 +956,23 @@ hipError_t launch_decode(const StepArgs& a) {
     p.G = G;
     p.HC = G / GW;
     p.scale_log2 = a.scale * 1.4426950408889634f;
-    // One wave per unit over the upper bound of units (4 waves per workgroup).
+    // One wave per unit over the upper bound of units (4 waves per
+    // workgroup), or with partition groups one workgroup per unit.
+    const int gp = decode_group_parts(G, a.head_dim);
     const int64_t units = a.lay.cap_dec * a.num_kv_heads * p.HC;
-    const int64_t grid64 = (units + 3) / 4;
+    const int64_t grid64 = gp > 1 ? units : (units + 3) / 4;
     if (grid64 <= 0) return hipSuccess;
     if (grid64 > INT32_MAX) return hipErrorInvalidValue;
     const int grid = (int)grid64;
     if (a.head_dim == 128) {
         const bool two = GW > 16;  // 32 heads per wave: two MFMA column groups
+        if (two != (gp == 1)) return hipErrorInvalidValue;  // grouping follows the column groups
         if (a.block_size == 16) {
-            if (two) hipLaunchKernelGGL((decode_mfma_kernel<16, 2>), dim3(grid), dim3(256), 0, a.stream, p);
-            else hipLaunchKernelGGL((decode_mfma_kernel<16, 1>), dim3(grid), dim3(256), 0, a.stream, p);
+            if (two) hipLaunchKernelGGL((decode_mfma_kernel<16, 2, 1>), dim3(grid), dim3(256), 0, a.stream, p);
+            else hipLaunchKernelGGL((decode_mfma_kernel<16, 1, 4>), dim3(grid), dim3(256), 0, a.stream, p);
         } else {
-            if (two) hipLaunchKernelGGL((decode_mfma_kernel<4, 2>), dim3(grid), dim3(256), 0, a.stream, p);
-            else hipLaunchKernelGGL((decode_mfma_kernel<4, 1>), dim3(grid), dim3(256), 0, a.stream, p);
+            if (two) hipLaunchKernelGGL((decode_mfma_kernel<4, 2, 1>), dim3(grid), dim3(256), 0, a.stream, p);
+            else hipLaunchKernelGGL((decode_mfma_kernel<4, 1, 4>), dim3(grid), dim3(256), 0, a.stream, p);
         }
     } else {
         if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);

@@ -45,12 +45,20 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int prefill_hpw(int G) { return G >= 4 ? 4 : G; }
 inline int prefill_span(int G) { return PREFILL_QW * (4 / prefill_hpw(G)); }
 
+// Decode partitions per work item: the matrix decode with at most 16 q heads
+// per wave gives a workgroup's four waves four consecutive partitions of one
+// (sequence, kv head) and combines them in LDS, so split-K partials exist
+// per 4 * DECODE_PART tokens; the other decode paths take one partition per
+// wave.
+inline int decode_group_parts(int G, int head_dim) { return (head_dim == 128 && G % 32 != 0) ? 4 : 1; }
+
 inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context_len,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
     WsLayout w{};
     const int G = num_q_heads / num_kv_heads;
     const int64_t parts = ((int64_t)max_context_len + 1 + DECODE_PART - 1) / DECODE_PART;
-    w.cap_dec = (int64_t)num_seqs * parts;
+    const int gp = decode_group_parts(G, head_dim);
+    w.cap_dec = (int64_t)num_seqs * ((parts + gp - 1) / gp);
     w.cap_pre = (int64_t)total_q / prefill_span(G) + num_seqs;
     size_t off = 0;
     w.hdr = off;        off = align_up(off + HDR_WORDS * 4, 256);

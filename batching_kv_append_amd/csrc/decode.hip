@@ -451,13 +451,12 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // NG: 16-column groups of q heads per wave (1, or 2 for 32 heads on one kv
 // head, as in MQA): the groups share every K fragment and the V^T tile, so
 // the partition's K/V is read once for all of them.
-// GP: partitions per work item.  GP = 1: each wave is one (partition, kv
-// head, head chunk).  GP = 4 (NG = 1): a workgroup is one (group of four
-// consecutive partitions, kv head, head chunk); wave w takes partition
-// 4 x group + w, and the last of the group's waves to finish combines their
-// four (max, sum, accumulator) in LDS, in wave order, into the output (a
-// sequence of at most four partitions) or into one partial per group.
-template <int BS, int NG, int GP>
+// A workgroup is one work item: a group of GP = 4 consecutive partitions of
+// one (sequence, kv head, head chunk).  Wave w takes partition 4 x group + w,
+// and the last of the group's waves to finish combines their (max, sum,
+// accumulator) in LDS, in wave order, into the output (a sequence of at most
+// four partitions) or into one split-K partial per group.
+template <int BS, int NG>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     constexpr int A = 128;
     constexpr int CPR = A / 8;              // 16-byte chunks per row
@@ -467,12 +466,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     static_assert(NT <= 64, "table slice must fit one VGPR");
     static_assert(BS % 4 == 0, "4 consecutive tokens must share a block");
 
-    static_assert(GP == 1 || (GP == 4 && NG == 1), "partition groups need one column group");
+    constexpr int GP = DECODE_GROUP;        // partitions per work item, one per wave
+    static_assert(GP == 4, "one partition per wave of a 256-thread workgroup");
 
     // per wave: V^T of one 32-token step, [dim][4 chunks of 8 tokens], 64 B
-    // rows; with GP = 4 it then holds the wave's accumulator for the combine
-    __shared__ uint4 sVt[4][A * 4];
-    __shared__ float sML[GP > 1 ? 4 : 1][2][16];  // per wave: column max, column total
+    // rows; after the loop it holds the wave's accumulators (NG x 8 KiB) for
+    // the combine
+    __shared__ uint4 sVt[GP][A * 4 * NG];
+    __shared__ float sML[GP][2][16 * NG];  // per wave: column max, column total
     __shared__ int arrived;                        // waves of the group done
 
     const int wave = threadIdx.x >> 6;
@@ -480,12 +481,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     const int col = lane & 15;  // head column
     const int g = lane >> 4;    // token group: tokens 4g..4g+3 of each 16-token block
     const int64_t n_units = (int64_t)P.hdr[HDR_N_DEC] * P.hkv * P.HC;
-    const int64_t u = GP > 1 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + wave;
-    if (u >= n_units) return;  // GP > 1: the whole workgroup
-    if constexpr (GP > 1) {
-        if (threadIdx.x == 0) arrived = 0;
-        __syncthreads();  // the only barrier: waves past the sequence leave below
-    }
+    const int64_t u = blockIdx.x;
+    if (u >= n_units) return;  // the whole workgroup
+    if (threadIdx.x == 0) arrived = 0;
+    __syncthreads();  // the only barrier: waves past the sequence leave below
     uint4* vt = &sVt[wave][0];
 
     const int GW = P.G / P.HC;  // heads of this wave (<= 16 * NG)
@@ -497,8 +496,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
     const int L = P.ctx[s] + 1;
     const int row = P.cu[s];
     const int nparts = (L + DECODE_PART - 1) / DECODE_PART;
-    const int part = GP > 1 ? it.y * GP + wave : it.y;
-    if (part >= nparts) return;  // GP > 1: the group runs past the sequence
+    const int part = it.y * GP + wave;
+    if (part >= nparts) return;  // the group runs past the sequence
     const int nact = min(GP, nparts - it.y * GP);  // waves of this group with work
     const int ngroups = (nparts + GP - 1) / GP;    // work items of the sequence
     const int t0 = part * DECODE_PART;
@@ -724,52 +723,56 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
             if (16 * ng + col < GW) write_out(ng, o[ng], 1.f / lt[ng]);
         return;
     }
-    if constexpr (GP == 1) {
-#pragma unroll
-        for (int ng = 0; ng < NG; ++ng)
-            if (16 * ng + col < GW) write_partial(ng, o[ng], m[ng], lt[ng]);
-    } else {
+    {
         // Combine the group in LDS.  Each wave leaves its column max and
         // total and its accumulator (in its own V^T tile, no longer read),
         // then counts itself in; the wave that arrives last combines the
         // group in wave order (fixed, so the result does not depend on which
         // wave that is).
         float4* mine = reinterpret_cast<float4*>(vt);
-        if (g == 0) {
-            sML[wave][0][col] = m[0];
-            sML[wave][1][col] = lt[0];
-        }
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            mine[dt * 64 + lane] = make_float4(o[0][dt][0], o[0][dt][1], o[0][dt][2], o[0][dt][3]);
+        for (int ng = 0; ng < NG; ++ng) {
+            if (g == 0) {
+                sML[wave][0][16 * ng + col] = m[ng];
+                sML[wave][1][16 * ng + col] = lt[ng];
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                mine[(ng * 8 + dt) * 64 + lane] =
+                    make_float4(o[ng][dt][0], o[ng][dt][1], o[ng][dt][2], o[ng][dt][3]);
+        }
         __threadfence_block();  // this wave's LDS writes before its arrival
         int before = 0;
         if (lane == 0) before = atomicAdd(&arrived, 1);
         before = __shfl(before, 0, 64);
         if (before != nact - 1) return;
         __threadfence_block();  // every other wave's writes after the last arrival
-        float mm = -INFINITY;
-        for (int w = 0; w < nact; ++w) mm = fmaxf(mm, sML[w][0][col]);
-        float ll = 0.f;
-        f32x4_t acc[8];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < nact; ++w) {
-            const float sc = __builtin_amdgcn_exp2f(sML[w][0][col] - mm);
-            ll += sc * sML[w][1][col];
-            const float4* src = reinterpret_cast<const float4*>(&sVt[w][0]);
+        for (int ng = 0; ng < NG; ++ng) {
+            const int c16 = 16 * ng + col;
+            float mm = -INFINITY;
+            for (int w = 0; w < nact; ++w) mm = fmaxf(mm, sML[w][0][c16]);
+            float ll = 0.f;
+            f32x4_t acc[8];
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const float4 v = src[dt * 64 + lane];
-                acc[dt][0] += sc * v.x;
-                acc[dt][1] += sc * v.y;
-                acc[dt][2] += sc * v.z;
-                acc[dt][3] += sc * v.w;
+            for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < nact; ++w) {
+                const float sc = __builtin_amdgcn_exp2f(sML[w][0][c16] - mm);
+                ll += sc * sML[w][1][c16];
+                const float4* src = reinterpret_cast<const float4*>(&sVt[w][0]);
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) {
+                    const float4 v = src[(ng * 8 + dt) * 64 + lane];
+                    acc[dt][0] += sc * v.x;
+                    acc[dt][1] += sc * v.y;
+                    acc[dt][2] += sc * v.z;
+                    acc[dt][3] += sc * v.w;
+                }
             }
-        }
-        if (col < GW) {
-            if (ngroups == 1) write_out(0, acc, 1.f / ll);
-            else write_partial(0, acc, mm, ll);
+            if (c16 < GW) {
+                if (ngroups == 1) write_out(ng, acc, 1.f / ll);
+                else write_partial(ng, acc, mm, ll);
+            }
         }
     }
 }
@@ -956,8 +959,8 @@ hipError_t launch_decode(const StepArgs& a) {
     p.G = G;
     p.HC = G / GW;
     p.scale_log2 = a.scale * 1.4426950408889634f;
-    // One wave per unit over the upper bound of units (4 waves per
-    // workgroup), or with partition groups one workgroup per unit.
+    // Matrix decode: one workgroup per unit (a group of four partitions)
+    // over the upper bound of units; head_dim 16: one wave per unit.
     const int gp = decode_group_parts(G, a.head_dim);
     const int64_t units = a.lay.cap_dec * a.num_kv_heads * p.HC;
     const int64_t grid64 = gp > 1 ? units : (units + 3) / 4;
@@ -966,13 +969,13 @@ hipError_t launch_decode(const StepArgs& a) {
     const int grid = (int)grid64;
     if (a.head_dim == 128) {
         const bool two = GW > 16;  // 32 heads per wave: two MFMA column groups
-        if (two != (gp == 1)) return hipErrorInvalidValue;  // grouping follows the column groups
+        if (gp != 4) return hipErrorInvalidValue;  // the matrix decode works in partition groups
         if (a.block_size == 16) {
-            if (two) hipLaunchKernelGGL((decode_mfma_kernel<16, 2, 1>), dim3(grid), dim3(256), 0, a.stream, p);
-            else hipLaunchKernelGGL((decode_mfma_kernel<16, 1, 4>), dim3(grid), dim3(256), 0, a.stream, p);
+            if (two) hipLaunchKernelGGL((decode_mfma_kernel<16, 2>), dim3(grid), dim3(256), 0, a.stream, p);
+            else hipLaunchKernelGGL((decode_mfma_kernel<16, 1>), dim3(grid), dim3(256), 0, a.stream, p);
         } else {
-            if (two) hipLaunchKernelGGL((decode_mfma_kernel<4, 2, 1>), dim3(grid), dim3(256), 0, a.stream, p);
-            else hipLaunchKernelGGL((decode_mfma_kernel<4, 1, 4>), dim3(grid), dim3(256), 0, a.stream, p);
+            if (two) hipLaunchKernelGGL((decode_mfma_kernel<4, 2>), dim3(grid), dim3(256), 0, a.stream, p);
+            else hipLaunchKernelGGL((decode_mfma_kernel<4, 1>), dim3(grid), dim3(256), 0, a.stream, p);
         }
     } else {
         if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);

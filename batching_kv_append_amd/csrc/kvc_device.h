@@ -45,12 +45,15 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int prefill_hpw(int G) { return G >= 4 ? 4 : G; }
 inline int prefill_span(int G) { return PREFILL_QW * (4 / prefill_hpw(G)); }
 
-// Decode partitions per work item: the matrix decode with at most 16 q heads
-// per wave gives a workgroup's four waves four consecutive partitions of one
-// (sequence, kv head) and combines them in LDS, so split-K partials exist
-// per 4 * DECODE_PART tokens; the other decode paths take one partition per
-// wave.
-inline int decode_group_parts(int G, int head_dim) { return (head_dim == 128 && G % 32 != 0) ? 4 : 1; }
+// Decode partitions per work item: the matrix decode (head_dim 128) gives a
+// workgroup's four waves four consecutive partitions of one (sequence, kv
+// head, head chunk) and combines them in LDS, so split-K partials exist per
+// 4 * DECODE_PART tokens; the head_dim 16 decode takes one partition per wave.
+constexpr int DECODE_GROUP = 4;  // partitions per matrix-decode workgroup (its four waves)
+inline int decode_group_parts(int G, int head_dim) {
+    (void)G;
+    return head_dim == 128 ? DECODE_GROUP : 1;
+}
 
 inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context_len,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {

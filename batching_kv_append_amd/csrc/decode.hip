@@ -456,8 +456,11 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // and the last of the group's waves to finish combines their (max, sum,
 // accumulator) in LDS, in wave order, into the output (a sequence of at most
 // four partitions) or into one split-K partial per group.
+// The two-group kernel is held to two waves per SIMD (at most 256 VGPRs; it
+// fits in 228 without spills): left free it takes about 300 and runs one wave
+// per SIMD, too few loads in flight for a memory-bound kernel.
 template <int BS, int NG>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(DecodeParams P) {
     constexpr int A = 128;
     constexpr int CPR = A / 8;              // 16-byte chunks per row
     constexpr int STEP = 32;                // tokens per matrix step

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const int64_t t = (int64_t)blockIdx.x * ROWS_PER_WG + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= total) return;
-    const int s = find_seq(cu, num_seqs, t);
+    const int s = find_seq(cu, num_seqs, t, lane);
     const int64_t p = t - cu[s];
     if (p < 0 || p >= seq_lens[s]) return;
     const int64_t lb = p / block_size;

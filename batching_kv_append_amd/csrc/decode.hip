@@ -98,6 +98,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     __shared__ int hist[COST_BUCKETS];
     __shared__ int carry[3];
     __shared__ int flags;
+    __shared__ int cu_ends[2];  // cu[0], cu[num_seqs], as the loop reads them
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     if (tid == 0) {
@@ -113,6 +114,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
         if (s < num_seqs) {
             const int r0 = cu[s], r1 = cu[s + 1];
             const int c = ctx[s];
+            if (s == 0) cu_ends[0] = r0;
+            if (s == num_seqs - 1) cu_ends[1] = r1;
             int q = r1 - r0;
             row0 = r0;
             // A sequence whose rows are not inside [0, total_q) or whose
@@ -197,7 +200,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
         pre_sorted[at] = item;
     }
     if (tid == 0) {
-        if (cu[0] != 0 || cu[num_seqs] != total_q) flags |= FLAG_CU_SEQLENS;
+        const int first = num_seqs > 0 ? cu_ends[0] : cu[0];
+        const int last = num_seqs > 0 ? cu_ends[1] : cu[0];
+        if (first != 0 || last != total_q) flags |= FLAG_CU_SEQLENS;
         hdr[HDR_N_DEC] = (int)min((int64_t)carry[0], cap_dec);
         hdr[HDR_N_PRE] = npre;
         hdr[HDR_N_MERGE] = carry[2];

@@ -116,13 +116,28 @@ __device__ __forceinline__ void set_flag(int32_t* hdr, int flag) {
     atomicOr(hdr + HDR_FLAGS, flag);
 }
 
-// Index of the sequence that owns row t: the largest s with cu[s] <= t.
+// Index of the sequence that owns row t: the largest s with cu[s] <= t,
+// found by the whole wave (every lane passes the same t).  Each round the 64
+// lanes probe 64 evenly spaced entries of the bracket [lo, hi] and a ballot
+// keeps the sub-bracket between the last probe <= t and the next one, so
+// S sequences take about log64(S) dependent loads (2 up to 4096) instead of
+// log2(S).  cu is non-decreasing; on any input the result stays in
+// [0, num_seqs - 1] and every round shrinks the bracket.
 template <typename T>
-__device__ __forceinline__ int find_seq(const T* cu, int num_seqs, int64_t t) {
+__device__ __forceinline__ int find_seq(const T* cu, int num_seqs, int64_t t, int lane) {
     int lo = 0, hi = num_seqs - 1;
     while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+        const int64_t span = hi - lo;
+        const int idx = lo + (int)(((int64_t)(lane + 1) * span + 63) / 64);  // lo < idx <= hi
+        const uint64_t le = __ballot((int64_t)cu[idx] <= t);
+        if (le == 0) {
+            hi = __shfl(idx, 0, 64) - 1;  // below the first probe
+        } else {
+            const int k = 63 - __builtin_clzll(le);  // last probe <= t
+            const int next = __shfl(idx, k < 63 ? k + 1 : 63, 64);
+            lo = __shfl(idx, k, 64);
+            hi = k < 63 ? next - 1 : hi;
+        }
     }
     return lo;
 }
@@ -138,7 +153,7 @@ __device__ __forceinline__ int append_row(const uint4* __restrict__ k_new,
                                           const int32_t* __restrict__ cu, const int32_t* __restrict__ ctx,
                                           int32_t num_seqs, int64_t t, int32_t hkv, int32_t head_dim,
                                           int32_t block_size, int lane) {
-    const int s = find_seq(cu, num_seqs, t);
+    const int s = find_seq(cu, num_seqs, t, lane);
     const int64_t p = (int64_t)ctx[s] + (t - cu[s]);
     const int64_t lb = p / block_size;
     if (p < 0 || lb >= max_blocks) return FLAG_TABLE_SHORT;

@@ -49,6 +49,7 @@ _sig("kvc_num_free_blocks", _I32, [_P])
 _sig("kvc_num_blocks", _I32, [_P])
 _sig("kvc_block_refcount", _I32, [_P, _I32])
 _sig("kvc_extend_table", ctypes.c_int, [_P, _P, _I32, ctypes.POINTER(_I32), _I64])
+_sig("kvc_extend_tables", ctypes.c_int, [_P, _P, _I32, _P, _P, _I32])
 _sig("kvc_cache_bytes", _I64, [_I64, _I32, _I32, _I32, _I32])
 _sig("kvc_allocator_block_size", _I32, [_P])
 _sig("kvc_cow_block", ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)])
@@ -86,7 +87,7 @@ KVC_ERR_HIP = -5
 EXPORTED = [
     "kvc_status_string", "kvc_last_error", "kvc_allocator_create", "kvc_allocator_destroy",
     "kvc_alloc_blocks", "kvc_share_blocks", "kvc_free_blocks", "kvc_num_free_blocks",
-    "kvc_num_blocks", "kvc_block_refcount", "kvc_extend_table", "kvc_cache_bytes",
+    "kvc_num_blocks", "kvc_block_refcount", "kvc_extend_table", "kvc_extend_tables", "kvc_cache_bytes",
     "kvc_cow_block", "kvc_fork_table", "kvc_copy_blocks", "kvc_allocator_block_size",
     "kvc_scheduler_create", "kvc_scheduler_destroy", "kvc_scheduler_add", "kvc_scheduler_step",
     "kvc_scheduler_complete", "kvc_scheduler_num_waiting", "kvc_scheduler_num_running",
@@ -215,6 +216,26 @@ def kvc_extend_table(alloc: Allocator, row, held: int, new_len: int) -> int:
     _check(_lib.kvc_extend_table(alloc.handle, row.ctypes.data_as(ctypes.c_void_p), row.size,
                                  ctypes.byref(h), new_len), "kvc_extend_table")
     return int(h.value)
+
+
+def kvc_extend_tables(alloc: Allocator, table, held, new_lens) -> None:
+    """Grow every row of a host table ([S, max_blocks] int32, modified in
+    place) to cover new_lens[s] tokens; held ([S] int32) is updated.  All or
+    nothing."""
+    import numpy as np
+    for name, a, dt, nd in (("table", table, np.int32, 2), ("held", held, np.int32, 1),
+                            ("new_lens", new_lens, np.int64, 1)):
+        if not (isinstance(a, np.ndarray) and a.dtype == dt and a.ndim == nd
+                and a.flags["C_CONTIGUOUS"]):
+            raise TypeError(f"{name}: expected a C-contiguous {np.dtype(dt).name} numpy array "
+                            f"with {nd} dims")
+    s = table.shape[0]
+    if held.shape[0] != s or new_lens.shape[0] != s:
+        raise ValueError("held and new_lens must have one entry per table row")
+    _check(_lib.kvc_extend_tables(alloc.handle, table.ctypes.data_as(ctypes.c_void_p),
+                                  table.shape[1], held.ctypes.data_as(ctypes.c_void_p),
+                                  new_lens.ctypes.data_as(ctypes.c_void_p), s),
+           "kvc_extend_tables")
 
 
 def kvc_allocator_block_size(alloc: Allocator) -> int:

@@ -150,6 +150,41 @@ extern "C" int kvc_extend_table(kvc_allocator* a, int32_t* row, int32_t max_bloc
     return KVC_OK;
 }
 
+// Just-in-time growth of a whole step's rows in one call (the same rule per
+// row as kvc_extend_table), all or nothing: every row is checked and the
+// blocks counted before any is taken.
+extern "C" int kvc_extend_tables(kvc_allocator* a, int32_t* table, int32_t max_blocks,
+                                 int32_t* held, const int64_t* new_lens, int32_t num_seqs) {
+    if (!a) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_extend_tables: allocator is NULL");
+    if (num_seqs < 0 || max_blocks < 0)
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_extend_tables: bad sizes");
+    if (num_seqs > 0 && (!table || !held || !new_lens))
+        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_extend_tables: NULL argument");
+    int64_t total = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        if (held[s] < 0 || held[s] > max_blocks || new_lens[s] < 0)
+            return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_extend_tables: bad sizes");
+        const int64_t need = (new_lens[s] + a->block_size - 1) / a->block_size;
+        if (need > max_blocks)
+            return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_extend_tables: row too short for new_len");
+        if (need > held[s]) total += need - held[s];
+    }
+    if (total > (int64_t)a->free_stack.size())
+        return kvc_fail(KVC_ERR_OOM, "kvc_extend_tables: not enough free blocks");
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t need = (new_lens[s] + a->block_size - 1) / a->block_size;
+        int32_t* row = table + (int64_t)s * max_blocks;
+        for (int64_t i = held[s]; i < need; ++i) {
+            const int32_t id = a->free_stack.back();
+            a->free_stack.pop_back();
+            a->refcount[id] = 1;
+            row[i] = id;
+        }
+        if (need > held[s]) held[s] = (int32_t)need;
+    }
+    return KVC_OK;
+}
+
 // Copy-on-write.  Sharing is done by editing tables (klklkl10086.github.io
 // kv_cache post, section "Paged Attention"), and a contiguous cache cannot
 // share at all (same post, section "连续内存分配", beam search).  A shared block

@@ -405,28 +405,29 @@ def stream_read_ceiling(gib=4):
 
 def host_alloc_cost(wl, steps, reps=20):
     """Host block allocation for the step (just-in-time table growth of every
-    sequence by its new tokens), timed on the product allocator; the blocks are
-    released after each repetition so every repetition sees the same state."""
+    sequence by its new tokens, one kvc_extend_tables call for all rows),
+    timed on the product allocator; the blocks are released after each
+    repetition so every repetition sees the same state."""
     import batching_kv_append_amd as kvc
     bs = wl.block_size
     st = steps[0]
     need = int(((st.context_lens.astype(np.int64) + st.q_lens + bs - 1) // bs).sum())
     alloc = kvc.Allocator(need + 64, bs)
     mb = st.block_table.shape[1]
-    rows = np.full((st.num_seqs, mb), -1, dtype=np.int32)
+    table = np.full((st.num_seqs, mb), -1, dtype=np.int32)
     held = np.zeros(st.num_seqs, dtype=np.int32)
-    for s in range(st.num_seqs):
-        held[s] = kvc.kvc_extend_table(alloc, rows[s], 0, int(st.context_lens[s]))
+    kvc.kvc_extend_tables(alloc, table, held, st.context_lens.astype(np.int64))
+    new_lens = (st.context_lens.astype(np.int64) + st.q_lens).astype(np.int64)
     ts = []
     for _ in range(reps):
         h2 = held.copy()
         t0 = time.perf_counter()
-        for s in range(st.num_seqs):
-            h2[s] = kvc.kvc_extend_table(alloc, rows[s], int(h2[s]),
-                                         int(st.context_lens[s] + st.q_lens[s]))
+        kvc.kvc_extend_tables(alloc, table, h2, new_lens)
         ts.append(time.perf_counter() - t0)
-        new = np.concatenate([rows[s, held[s]:h2[s]] for s in range(st.num_seqs)])
+        new = np.concatenate([table[s, held[s]:h2[s]] for s in range(st.num_seqs)])
         kvc.kvc_free_blocks(alloc, new)
+        table[h2 > held] = np.where(np.arange(mb)[None, :] < held[h2 > held][:, None],
+                                    table[h2 > held], -1)
     alloc.close()
     return float(np.median(ts) * 1e6)
 

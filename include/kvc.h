@@ -136,6 +136,15 @@ int32_t kvc_block_refcount(const kvc_allocator* a, int32_t id);
  * than max_blocks entries. */
 int kvc_extend_table(kvc_allocator* a, int32_t* row, int32_t max_blocks,
                      int32_t* held, int64_t new_len);
+/* The same growth for every row of a step's table at once: row s of `table`
+ * ([num_seqs][max_blocks] int32, host) holds held[s] valid ids and is grown to
+ * cover new_lens[s] tokens; held[s] is updated.  All or nothing for the whole
+ * batch: on any error (KVC_ERR_INVALID_ARG for a bad size or a row too short,
+ * KVC_ERR_OOM when the free blocks do not cover all rows) no row and no
+ * block changes.  For callers that grow every running sequence per step,
+ * one call instead of one per sequence. */
+int kvc_extend_tables(kvc_allocator* a, int32_t* table, int32_t max_blocks, int32_t* held,
+                      const int64_t* new_lens, int32_t num_seqs);
 
 /* Copy-on-write of one block before a write into it (a shared block must
  * not change under its other sharers; sharing by table edits, klklkl10086

@@ -60,6 +60,21 @@ int main() {
     CHECK(kvc_extend_table(a, row.data(), 8, &held, 16) == KVC_OK && held == 1);
     CHECK(kvc_extend_table(a, row.data(), 8, &held, 17) == KVC_OK && held == 2);
     CHECK(kvc_extend_table(a, row.data(), 8, &held, 129) == KVC_ERR_INVALID_ARG && held == 2);
+    {  // the batched form: two rows at once, then all or nothing on a too-short row
+        std::vector<int32_t> tab(2 * 8, -1);
+        int32_t hs[2] = {0, 0};
+        const int64_t lens[2] = {17, 33};
+        const int free0 = kvc_num_free_blocks(a);
+        CHECK(kvc_extend_tables(a, tab.data(), 8, hs, lens, 2) == KVC_OK && hs[0] == 2 && hs[1] == 3);
+        CHECK(kvc_num_free_blocks(a) == free0 - 5);
+        const int64_t too_long[2] = {20, 8 * 16 + 1};
+        CHECK(kvc_extend_tables(a, tab.data(), 8, hs, too_long, 2) == KVC_ERR_INVALID_ARG);
+        CHECK(hs[0] == 2 && hs[1] == 3 && kvc_num_free_blocks(a) == free0 - 5);
+        CHECK(kvc_free_blocks(a, tab.data(), 2) == KVC_OK);
+        CHECK(kvc_free_blocks(a, tab.data() + 8, 3) == KVC_OK);
+        CHECK(kvc_num_free_blocks(a) == free0);
+        invariants(a);
+    }
     // random churn
     std::mt19937 rng(1);
     std::vector<int32_t> live;

@@ -49,6 +49,45 @@ def test_just_in_time_growth(kvc):
         kvc.kvc_extend_table(a, row, held, 129)
 
 
+def test_extend_tables_batch(kvc):
+    """One call grows every row exactly as one call per row does, and is all
+    or nothing: too few free blocks or a row too short change nothing."""
+    rng = np.random.default_rng(5)
+    s, mb, bs = 40, 12, 16
+    ctx = rng.integers(0, 150, size=s)
+    new = ctx + rng.integers(0, 40, size=s)
+    a1, a2 = kvc.Allocator(600, bs), kvc.Allocator(600, bs)
+    t1 = np.full((s, mb), -1, np.int32)
+    t2 = t1.copy()
+    h1 = np.zeros(s, np.int32)
+    h2 = np.zeros(s, np.int32)
+    for i in range(s):  # the cached contexts first, row by row in both
+        h1[i] = kvc.kvc_extend_table(a1, t1[i], 0, int(ctx[i]))
+        h2[i] = kvc.kvc_extend_table(a2, t2[i], 0, int(ctx[i]))
+    for i in range(s):
+        h1[i] = kvc.kvc_extend_table(a1, t1[i], int(h1[i]), int(new[i]))
+    kvc.kvc_extend_tables(a2, t2, h2, new.astype(np.int64))
+    assert np.array_equal(t1, t2) and np.array_equal(h1, h2)
+    assert kvc.kvc_num_free_blocks(a1) == kvc.kvc_num_free_blocks(a2)
+    assert (h2 == (new + bs - 1) // bs).all()
+    # too few free blocks for the batch: nothing changes
+    free0, t_before, h_before = kvc.kvc_num_free_blocks(a2), t2.copy(), h2.copy()
+    more = new + 16 * (free0 // s + 1)
+    more = np.minimum(more, mb * bs).astype(np.int64)
+    if int(((more + bs - 1) // bs - h2).sum()) > free0:
+        with pytest.raises(kvc.KvcError):
+            kvc.kvc_extend_tables(a2, t2, h2, more)
+        assert kvc.kvc_num_free_blocks(a2) == free0
+        assert np.array_equal(t2, t_before) and np.array_equal(h2, h_before)
+    # a row that would need more than max_blocks entries: nothing changes
+    bad = new.astype(np.int64).copy()
+    bad[-1] = mb * bs + 1
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_extend_tables(a2, t2, h2, bad)
+    assert np.array_equal(t2, t_before) and np.array_equal(h2, h_before)
+    assert kvc.kvc_num_free_blocks(a2) == free0
+
+
 def test_prefix_sharing_footprint(kvc):
     """16 sequences share a 2048-token prefix (128 blocks) written once, each
     with a 256-token suffix: 128 + 16*16 = 384 blocks instead of 16*144."""

@@ -589,6 +589,9 @@ def main():
         prefill = {"flops_per_step": alg["prefill_flops"], "visible_pairs_per_head":
                    alg["prefill_pairs"], "kernel_us": pre_us, "tflops": tf,
                    "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+        if decode:
+            prefill["note"] = ("runs on the side stream under the decode: kernel_us is its "
+                               "window beside the decode, not its own speed")
 
     launches = len(calls)  # per step; each call launches each kernel at most once
     if decode and (not prefill or dec_us >= pre_us):

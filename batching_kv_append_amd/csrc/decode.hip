@@ -5,24 +5,23 @@
 // (klklkl10086.github.io kv_cache post, section on the decode bottleneck: the
 // decode stage is limited by memory access; clvsit.github.io AWS SageMaker
 // page: every step moves the parameters and the cache into the compute
-// units).  The kernel therefore aims at HBM bandwidth:
+// units).  The kernels therefore aim at HBM bandwidth:
 //   * a sequence's context is cut into fixed partitions of DECODE_PART tokens
 //     (split-K), so even a short batch of long contexts yields thousands of
-//     independent work units; the partial softmax states are combined by an
-//     exact log-sum-exp merge (an exact regrouping of the row-wise softmax of
-//     the "Attention" section of the continuous-batching article);
-//   * one wavefront per (sequence, partition, kv head, head chunk): the GW
-//     query heads that share a kv head (GQA, e2hang/Notes "MQA与GQA") are
-//     served from one read of K/V;
-//   * 16 lanes own one 128-dim bf16 token row (16 B = 8 values each), so each
-//     load instruction reads 4 whole rows = 1 KiB contiguous from one block
-//     (the block table gives each 16-token block as one 4 KiB run per head);
-//   * q.k partial dots are reduced across the 16 lanes with DPP row
-//     operations; softmax is online per lane group, with one cross-group
-//     merge per work unit.
-// The planning kernel lists the work units on the device, so the host needs no
-// copy of the lengths; each wave takes one unit, and the hardware dispatcher
-// hands the next workgroup to whichever compute unit frees up first.
+//     independent pieces of work; the partial softmax states are combined by
+//     an exact log-sum-exp merge (an exact regrouping of the row-wise softmax
+//     of the "Attention" section of the continuous-batching article);
+//   * the GW query heads that share a kv head (GQA, e2hang/Notes "MQA与GQA")
+//     are served from one read of K/V;
+//   * head_dim 128 (decode_mfma_kernel): a workgroup takes four consecutive
+//     partitions of one (sequence, kv head, head chunk), one per wave, scores
+//     and P.V on bf16 MFMA, and the group's four states are combined in LDS,
+//     so split-K partials (and the merge) exist per 1024 tokens;
+//   * head_dim 16 (decode_kernel): one wave per partition, 16 lanes per
+//     token row, dot products reduced with DPP row operations.
+// The planning kernel lists the work items on the device, so the host needs
+// no copy of the lengths, and the hardware dispatcher hands the next
+// workgroup to whichever compute unit frees up first.
 #include <hip/hip_runtime.h>
 
 #include "kvc_launch.h"

@@ -438,16 +438,28 @@ KERNEL_SOURCES = {
 }
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter summaries in profiles/,
-    or None when none was taken on the kernel's current source."""
-    import glob
+def source_digest(kernel):
+    """First 16 hex digits of a SHA-256 over the kernel's sources with the
+    comments and blank lines removed (so a comment edit keeps the counters
+    that were taken on the same code)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    key = f"traffic {kernel} src_sha256_16={h.hexdigest()[:16]} "
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", "", text)                 # line comments
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode("utf-8"))
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summaries in profiles/,
+    or None when none was taken on the kernel's current code."""
+    import glob
+    key = f"traffic {kernel} src_sha256_16={source_digest(kernel)} "
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as fh:
             for line in fh:

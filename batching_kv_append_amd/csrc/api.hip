@@ -380,6 +380,16 @@ extern "C" int kvc_paged_attention_varlen(
     a.lay = lay;
     a.stream = st;
 
+    // Rows of one new token (decode) can be ruled out from the host sizes
+    // alone: with d such sequences and every other one holding at most
+    // max_q_len rows, total_q <= d + (num_seqs - d) * max_q_len. When that
+    // leaves d = 0 the step is chunks only, and it skips the decode and merge
+    // launches and the side-stream fork. (A call whose cu_seqlens_q break the
+    // host sizes is flagged by the planner either way.)
+    const bool has_decode =
+        max_q_len < 2 ||
+        (int64_t)num_seqs * max_q_len - total_q >= (int64_t)max_q_len - 1;
+
     std::unique_lock<std::mutex> prof_lk(g_prof_mu);
     // planning and append share one launch (counted under "plan")
     prof_mark(KVC_PROF_PLAN, false, st);
@@ -387,7 +397,8 @@ extern "C" int kvc_paged_attention_varlen(
     prof_mark(KVC_PROF_PLAN, true, st);
     // The prefill kernel (rows of chunks with >= 2 new tokens) runs on the side
     // stream when there is one, concurrently with decode and merge.
-    SideStream* ss = (max_q_len >= 2 && overlap_enabled()) ? side_stream() : nullptr;
+    SideStream* ss =
+        (max_q_len >= 2 && has_decode && overlap_enabled()) ? side_stream() : nullptr;
     std::unique_lock<std::mutex> side_lk;
     if (ss) side_lk = std::unique_lock<std::mutex>(ss->mu);
     if (e == hipSuccess && max_q_len >= 2) {
@@ -402,13 +413,15 @@ extern "C" int kvc_paged_attention_varlen(
         prof_mark(KVC_PROF_PREFILL, true, ap.stream);
         if (ss && e == hipSuccess) e = hipEventRecord(ss->join, ss->stream);
     }
-    prof_mark(KVC_PROF_DECODE, false, st);
-    if (e == hipSuccess) e = kvc::launch_decode(a);
-    prof_mark(KVC_PROF_DECODE, true, st);
-    prof_mark(KVC_PROF_MERGE, false, st);
-    if (e == hipSuccess) e = kvc::launch_merge(a);
-    prof_mark(KVC_PROF_MERGE, true, st);
-    if (ss && max_q_len >= 2) {
+    if (has_decode) {
+        prof_mark(KVC_PROF_DECODE, false, st);
+        if (e == hipSuccess) e = kvc::launch_decode(a);
+        prof_mark(KVC_PROF_DECODE, true, st);
+        prof_mark(KVC_PROF_MERGE, false, st);
+        if (e == hipSuccess) e = kvc::launch_merge(a);
+        prof_mark(KVC_PROF_MERGE, true, st);
+    }
+    if (ss) {
         // join even after a failed launch, so the caller's stream never runs
         // ahead of work already queued on the side stream
         hipError_t ej = hipStreamWaitEvent(st, ss->join, 0);

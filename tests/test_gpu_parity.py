@@ -55,6 +55,13 @@ SMALL = [
     ("a16_mixed", [(0, 7), (4, 3), (7, 1), (30, 1), (100, 40), (0, 1), (257, 1)], 1, 1, 16, 4),
     ("a16_gqa2_bs16", [(0, 7), (4, 3), (7, 1), (30, 1), (100, 40), (600, 1)], 4, 2, 16, 16),
     ("a16_gqa4_bs4", [(0, 70), (33, 1), (2, 2)], 4, 1, 16, 4),
+    # The host rules decode rows out when total_q > (num_seqs - 1) * max_q_len + 1.
+    # At the bound one decode row is still possible and must be served; one row
+    # past it the step holds chunks only.
+    ("bound_one_decode", [(50, 4), (300, 1)], 8, 2, 128, 16),
+    ("bound_chunks_only", [(50, 4), (300, 2)], 8, 2, 128, 16),
+    ("bound_empty_seq", [(50, 4), (300, 0), (10, 3), (2000, 1)], 8, 2, 128, 16),
+    ("a16_bound_one_decode", [(9, 3), (40, 1)], 2, 1, 16, 4),
 ]
 
 

@@ -13,10 +13,12 @@
 //     of the "Attention" section of the continuous-batching article);
 //   * the GW query heads that share a kv head (GQA, e2hang/Notes "MQA与GQA")
 //     are served from one read of K/V;
-//   * head_dim 128 (decode_mfma_kernel): a workgroup takes four consecutive
-//     partitions of one (sequence, kv head, head chunk), one per wave, scores
-//     and P.V on bf16 MFMA, and the group's four states are combined in LDS,
-//     so split-K partials (and the merge) exist per 1024 tokens;
+//   * head_dim 128 (decode_mfma_kernel): a sequence is cut into
+//     ceil(L / 1024) work items of equal length, and a workgroup takes one
+//     item of one (sequence, kv head, head chunk), a quarter of it per wave
+//     (at most one partition), scores and P.V on bf16 MFMA; the four states
+//     are combined in LDS, so split-K partials (and the merge) exist per
+//     item;
 //   * head_dim 16 (decode_kernel): one wave per partition, 16 lanes per
 //     token row, dot products reduced with DPP row operations.
 // The planning kernel lists the work items on the device, so the host needs
@@ -455,11 +457,13 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // NG: 16-column groups of q heads per wave (1, or 2 for 32 heads on one kv
 // head, as in MQA): the groups share every K fragment and the V^T tile, so
 // the partition's K/V is read once for all of them.
-// A workgroup is one work item: a group of GP = 4 consecutive partitions of
-// one (sequence, kv head, head chunk).  Wave w takes partition 4 x group + w,
-// and the last of the group's waves to finish combines their (max, sum,
-// accumulator) in LDS, in wave order, into the output (a sequence of at most
-// four partitions) or into one split-K partial per group.
+// A workgroup is one work item of one (sequence, kv head, head chunk).  The
+// sequence's ceil(L / (GP x DECODE_PART)) items split it evenly, and wave w
+// takes the w-th quarter of its item (a multiple of 32 tokens, at most one
+// partition), so a short sequence keeps all four waves busy for a short time
+// instead of one wave for a long one.  The last of the item's waves to finish
+// combines their (max, sum, accumulator) in LDS, in wave order, into the
+// output (a sequence of one item) or into one split-K partial per item.
 // The two-group kernel is held to two waves per SIMD (at most 256 VGPRs; it
 // fits in 228 without spills): left free it takes about 300 and runs one wave
 // per SIMD, too few loads in flight for a memory-bound kernel.
@@ -473,8 +477,8 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     static_assert(NT <= 64, "table slice must fit one VGPR");
     static_assert(BS % 4 == 0, "4 consecutive tokens must share a block");
 
-    constexpr int GP = DECODE_GROUP;        // partitions per work item, one per wave
-    static_assert(GP == 4, "one partition per wave of a 256-thread workgroup");
+    constexpr int GP = DECODE_GROUP;        // waves per work item (at most a partition each)
+    static_assert(GP == 4, "one quarter of an item per wave of a 256-thread workgroup");
 
     // per wave: V^T of one 32-token step, [dim][4 chunks of 8 tokens], 64 B
     // rows; after the loop it holds the wave's accumulators (NG x 8 KiB) for
@@ -502,13 +506,19 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     const int s = it.x;
     const int L = P.ctx[s] + 1;
     const int row = P.cu[s];
-    const int nparts = (L + DECODE_PART - 1) / DECODE_PART;
-    const int part = it.y * GP + wave;
-    if (part >= nparts) return;  // the group runs past the sequence
-    const int nact = min(GP, nparts - it.y * GP);  // waves of this group with work
-    const int ngroups = (nparts + GP - 1) / GP;    // work items of the sequence
-    const int t0 = part * DECODE_PART;
-    const int t1 = min(L, t0 + DECODE_PART);
+    // The sequence's items split it evenly: each covers span tokens (the
+    // last one fewer) and each wave a quarter of that, a multiple of STEP
+    // tokens and at most one partition.  Item count and split depend only on
+    // the sequence's own length.
+    const int ngroups = (L + GP * DECODE_PART - 1) / (GP * DECODE_PART);  // work items of the sequence
+    const int per_wave = ((L + GP * ngroups - 1) / (GP * ngroups) + STEP - 1) / STEP * STEP;
+    const int span = GP * per_wave;
+    const int i0 = it.y * span;
+    const int t0 = i0 + wave * per_wave;
+    if (t0 >= L) return;  // the item runs past the sequence
+    const int nact = min(GP, (L - i0 + per_wave - 1) / per_wave);  // waves of this item with work
+    const int nparts = ngroups == 1 ? nact : 2;  // 1: one wave holds the whole sequence
+    const int t1 = min(L, t0 + per_wave);
     const int h0 = kvh * P.G + hc * GW;
     const float cs = P.scale_log2;
     const bool pos_scale = cs > 0.f;

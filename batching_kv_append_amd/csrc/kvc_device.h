@@ -45,10 +45,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int prefill_hpw(int G) { return G >= 4 ? 4 : G; }
 inline int prefill_span(int G) { return PREFILL_QW * (4 / prefill_hpw(G)); }
 
-// Decode partitions per work item: the matrix decode (head_dim 128) gives a
-// workgroup's four waves four consecutive partitions of one (sequence, kv
-// head, head chunk) and combines them in LDS, so split-K partials exist per
-// 4 * DECODE_PART tokens; the head_dim 16 decode takes one partition per wave.
+// Decode partitions per work item: the matrix decode (head_dim 128) cuts a
+// sequence into ceil(L / (4 * DECODE_PART)) equal items, gives each of a
+// workgroup's four waves a quarter of one item and combines them in LDS, so
+// split-K partials exist per item; the head_dim 16 decode takes one partition
+// per wave.
 constexpr int DECODE_GROUP = 4;  // partitions per matrix-decode workgroup (its four waves)
 inline int decode_group_parts(int G, int head_dim) {
     (void)G;

@@ -38,6 +38,7 @@ namespace {
 constexpr int PLAN_THREADS = 1024;
 
 constexpr int COST_BUCKETS = 1024;  // prefill cost histogram (key tiles, clamped)
+constexpr int DEC_BUCKETS = DECODE_PART / 32;  // decode order: 32-token steps per wave
 
 struct PrepParams {
     // planning
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     __shared__ int carry[3];
     __shared__ int flags;
     __shared__ int cu_ends[2];  // cu[0], cu[num_seqs], as the loop reads them
+    __shared__ int dec_off[DEC_BUCKETS];  // decode items per bucket, then offsets
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     if (tid == 0) {
@@ -108,67 +110,125 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
         hdr[HDR_FLAGS] = 0;
     }
     for (int b = tid; b < COST_BUCKETS; b += PLAN_THREADS) hist[b] = 0;
+    if (tid < DEC_BUCKETS) dec_off[tid] = 0;
     __syncthreads();
+    // The lengths of sequence s, checked against the host bounds.  A
+    // sequence whose rows are not inside [0, total_q) or whose lengths break
+    // the host bounds is skipped (and flagged): no later kernel touches its
+    // rows, so garbage lengths can never move an access out of bounds.
+    // Returns q (0 when skipped); sets c and the first row.
+    auto seq_lengths = [&](int s, int& c, int& row0, bool flag) -> int {
+        const int r0 = cu[s], r1 = cu[s + 1];
+        c = ctx[s];
+        row0 = r0;
+        if (r0 < 0 || r1 < r0 || r1 > total_q || c < 0) {
+            if (flag) atomicOr(&flags, FLAG_CU_SEQLENS);
+            return 0;
+        }
+        if (c > max_context_len || r1 - r0 > max_q_len) {
+            if (flag) atomicOr(&flags, FLAG_CAPACITY);
+            return 0;
+        }
+        return r1 - r0;
+    };
+    // Decode items of a sequence with c cached tokens, and the bucket that
+    // orders them: the matrix decode gives each wave a quarter of an item,
+    // and items with longer quarters run first, so short ones fill the end
+    // of the launch.
+    auto decode_items = [&](int c, int& bucket) -> int {
+        const int L = c + 1;
+        if (gp == 1) {
+            bucket = 0;
+            return (L + DECODE_PART - 1) / DECODE_PART;
+        }
+        const int ng = (L + gp * DECODE_PART - 1) / (gp * DECODE_PART);
+        const int per_wave = ((L + gp * ng - 1) / (gp * ng) + 31) / 32;  // in 32-token steps
+        bucket = min(per_wave, DEC_BUCKETS) - 1;
+        return ng;
+    };
+    // Pass 1: count decode items per bucket; list the prefill items.
     for (int base = 0; base < num_seqs; base += PLAN_THREADS) {
         const int s = base + tid;
-        int nd = 0, np = 0, nm = 0, row0 = 0;
+        int nd = 0, np = 0;
         if (s < num_seqs) {
-            const int r0 = cu[s], r1 = cu[s + 1];
-            const int c = ctx[s];
-            if (s == 0) cu_ends[0] = r0;
-            if (s == num_seqs - 1) cu_ends[1] = r1;
-            int q = r1 - r0;
-            row0 = r0;
-            // A sequence whose rows are not inside [0, total_q) or whose
-            // lengths break the host bounds is skipped (and flagged): no
-            // later kernel touches its rows, so garbage lengths can never
-            // move an access out of bounds.
-            if (r0 < 0 || r1 < r0 || r1 > total_q || c < 0) {
-                atomicOr(&flags, FLAG_CU_SEQLENS);
-                q = 0;
-            } else if (c > max_context_len || q > max_q_len) {
-                atomicOr(&flags, FLAG_CAPACITY);
-                q = 0;
-            }
+            int c, row0;
+            const int q = seq_lengths(s, c, row0, true);
+            if (s == 0) cu_ends[0] = row0;
+            if (s == num_seqs - 1) cu_ends[1] = cu[s + 1];
             if (q == 1) {
-                const int parts = (c + 1 + DECODE_PART - 1) / DECODE_PART;
-                nd = (parts + gp - 1) / gp;  // work items of gp partitions
-                nm = nd > 1;
+                int b;
+                nd = decode_items(c, b);
+                atomicAdd(&dec_off[b], nd);
             } else if (q >= 2) {
                 np = (q + span - 1) / span;
             }
         }
         // exclusive offsets: scan inside the wave, then the wave totals
-        const int id = wave_scan(nd, lane), ip = wave_scan(np, lane), im = wave_scan(nm, lane);
+        const int id = wave_scan(nd, lane), ip = wave_scan(np, lane);
         if (lane == 63) {
             wsum[0][wave] = id;
             wsum[1][wave] = ip;
-            wsum[2][wave] = im;
         }
         __syncthreads();
-        int od = carry[0] + id - nd, op = carry[1] + ip - np, om = carry[2] + im - nm;
-        for (int w = 0; w < wave; ++w) {
-            od += wsum[0][w];
-            op += wsum[1][w];
-            om += wsum[2][w];
-        }
+        int op = carry[1] + ip - np;
+        for (int w = 0; w < wave; ++w) op += wsum[1][w];
         if (s < num_seqs) {
-            for (int j = 0; j < nd; ++j) {
-                if (od + j < cap_dec) dec_items[od + j] = make_int2(s, j);
-                else atomicOr(&flags, FLAG_CAPACITY);
-            }
             // heavier (later) position tiles first
             for (int j = 0; j < np; ++j) {
                 if (op + j < cap_pre) pre_items[op + j] = make_int2(s, np - 1 - j);
                 else atomicOr(&flags, FLAG_CAPACITY);
             }
-            if (nm) merge_list[om] = make_int4(s, od, nd, row0);
         }
         __syncthreads();  // every thread has read carry and wsum
-        if (tid < 3) {
+        if (tid < 2) {
             int t = 0;
             for (int w = 0; w < WAVES; ++w) t += wsum[tid][w];
             carry[tid] += t;
+        }
+        __syncthreads();
+    }
+    // Bucket offsets, longest quarters first.
+    if (tid == 0) {
+        int o = 0;
+        for (int b = DEC_BUCKETS - 1; b >= 0; --b) {
+            const int n = dec_off[b];
+            dec_off[b] = o;
+            o += n;
+        }
+    }
+    __syncthreads();
+    // Pass 2: place each decode sequence's items (consecutive, in order, at
+    // a position taken from its bucket) and write its merge descriptor.  The
+    // order inside a bucket only changes which workgroup starts first: an
+    // item's result does not depend on its position.
+    for (int base = 0; base < num_seqs; base += PLAN_THREADS) {
+        const int s = base + tid;
+        int nd = 0, nm = 0, b = 0, row0 = 0;
+        if (s < num_seqs) {
+            int c;
+            if (seq_lengths(s, c, row0, false) == 1) {
+                nd = decode_items(c, b);
+                nm = nd > 1;
+            }
+        }
+        const int im = wave_scan(nm, lane);
+        if (lane == 63) wsum[2][wave] = im;
+        __syncthreads();
+        int om = carry[2] + im - nm;
+        for (int w = 0; w < wave; ++w) om += wsum[2][w];
+        if (nd > 0) {
+            const int pos = atomicAdd(&dec_off[b], nd);
+            for (int j = 0; j < nd; ++j) {
+                if (pos + j < cap_dec) dec_items[pos + j] = make_int2(s, j);
+                else atomicOr(&flags, FLAG_CAPACITY);
+            }
+            if (nm) merge_list[om] = make_int4(s, pos, nd, row0);
+        }
+        __syncthreads();  // every thread has read carry and wsum
+        if (tid == 0) {
+            int t = 0;
+            for (int w = 0; w < WAVES; ++w) t += wsum[2][w];
+            carry[2] += t;
         }
         __syncthreads();
     }

@@ -70,6 +70,17 @@ def test_small(kvc, orc, name, specs, hq, hkv, a, bs):
     _case(kvc, orc, name, specs, hq, hkv, a, bs)
 
 
+def test_planner_beyond_its_lds_cache(kvc, orc):
+    """More sequences (2500) and more prefill work items (4200) than the
+    planner keeps in LDS (2048 of each), in shuffled order, so both its cached
+    and its global-memory paths place work."""
+    rng = np.random.default_rng(11)
+    specs = [(int(c), 33) for c in rng.integers(0, 40, 2100)]
+    specs += [(int(c), 1) for c in rng.integers(0, 1500, 400)]
+    specs = [specs[i] for i in rng.permutation(len(specs))]
+    _case(kvc, orc, "many_seqs", specs, 8, 2, 128, 16)
+
+
 def test_scale_variants(kvc, orc):
     _case(kvc, orc, "scale0", [(20, 1), (0, 40), (300, 1)], 4, 2, 128, 16, scale=0.0)
     _case(kvc, orc, "scale_big", [(20, 1), (0, 40), (300, 1)], 4, 2, 128, 16, scale=0.5)

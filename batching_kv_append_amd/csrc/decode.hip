@@ -645,6 +645,17 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             for (int ks = 0; ks < 4; ++ks) kb[b][ks] = kp[ks * 4];
         }
         // ---- V: token groups g and g+4 (4 tokens each) x chunk col --------
+        // Each V load instruction reads whole 256-byte rows, so V is streamed
+        // with the non-temporal hint: the lines are used once and do not
+        // displace other data in L2 (about 7 % more bandwidth).  Both branches
+        // load through the same helper, since merging a non-temporal load with
+        // a plain one drops the hint.  K stays on plain loads: one K load
+        // instruction covers half of each 128-byte line, and the hint made the
+        // second half miss.
+        auto v_stream = [&](const uint4* ptr) -> uint4 {
+            return __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(ptr)));
+        };
         uint4 vb[2][4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -655,11 +666,11 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             const uint4* vp = P.v_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col;
             if (tc + 4 * tg + 3 < t1) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) vb[hh][j] = vp[j * CPR];
+                for (int j = 0; j < 4; ++j) vb[hh][j] = v_stream(vp + j * CPR);
             } else {  // rows past the end repeat the last row (their weight is 0)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    vb[hh][j] = vp[(min(tc + 4 * tg + j, t1 - 1) - t) * CPR];
+                    vb[hh][j] = v_stream(vp + (min(tc + 4 * tg + j, t1 - 1) - t) * CPR);
             }
         }
 

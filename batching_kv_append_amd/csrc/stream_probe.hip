@@ -8,6 +8,9 @@
 //                    per block group: the decode kernel's access pattern (one kv
 //                    head of a 16-token block of 128 bf16 dims is 4 KiB)
 //
+// Either reads with plain loads or with the non-temporal hint (data used once,
+// kept from displacing other lines in L2), which streams faster on gfx950.
+//
 // Both reduce what they read into one word per thread so that the loads are
 // not removed; `out` needs grid * 256 uint32 words.
 #include <hip/hip_runtime.h>
@@ -15,7 +18,17 @@
 
 namespace {
 
-template <int U>
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint4* p) {
+    if constexpr (NT)
+        return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+    else
+        return *p;
+}
+
+template <int U, bool NT>
 __global__ __launch_bounds__(256) void seq_read(const uint4* __restrict__ p, int64_t n16,
                                                 uint32_t* __restrict__ out) {
     const int64_t stride = (int64_t)gridDim.x * 256;
@@ -25,7 +38,7 @@ __global__ __launch_bounds__(256) void seq_read(const uint4* __restrict__ p, int
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int64_t i = base + k * stride;
-            v[k] = i < n16 ? p[i] : make_uint4(0, 0, 0, 0);
+            v[k] = i < n16 ? ld16<NT>(p + i) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
@@ -34,7 +47,7 @@ __global__ __launch_bounds__(256) void seq_read(const uint4* __restrict__ p, int
 }
 
 // Wave w reads blocks perm[w*U .. w*U+U-1], then skips ahead by all waves.
-template <int U>
+template <int U, bool NT>
 __global__ __launch_bounds__(256) void block_read(const uint4* __restrict__ p,
                                                   const int32_t* __restrict__ perm, int64_t nblk,
                                                   uint32_t* __restrict__ out) {
@@ -50,7 +63,7 @@ __global__ __launch_bounds__(256) void block_read(const uint4* __restrict__ p,
             const int64_t pb = b < nblk ? perm[b] : 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                v[k][j] = b < nblk ? p[pb * 256 + j * 64 + lane] : make_uint4(0, 0, 0, 0);
+                v[k][j] = b < nblk ? ld16<NT>(p + pb * 256 + j * 64 + lane) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int k = 0; k < U; ++k)
@@ -60,35 +73,51 @@ __global__ __launch_bounds__(256) void block_read(const uint4* __restrict__ p,
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+
+template <bool NT>
+hipError_t launch_seq(const uint4* p, int64_t n16, uint32_t* out, int grid, int unroll, hipStream_t st) {
+    switch (unroll) {
+        case 4: hipLaunchKernelGGL((seq_read<4, NT>), dim3(grid), dim3(256), 0, st, p, n16, out); break;
+        case 8: hipLaunchKernelGGL((seq_read<8, NT>), dim3(grid), dim3(256), 0, st, p, n16, out); break;
+        case 16: hipLaunchKernelGGL((seq_read<16, NT>), dim3(grid), dim3(256), 0, st, p, n16, out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <bool NT>
+hipError_t launch_block(const uint4* p, const int32_t* perm, int64_t nblk, uint32_t* out, int grid,
+                        int unroll, hipStream_t st) {
+    switch (unroll) {
+        case 2: hipLaunchKernelGGL((block_read<2, NT>), dim3(grid), dim3(256), 0, st, p, perm, nblk, out); break;
+        case 4: hipLaunchKernelGGL((block_read<4, NT>), dim3(grid), dim3(256), 0, st, p, perm, nblk, out); break;
+        case 8: hipLaunchKernelGGL((block_read<8, NT>), dim3(grid), dim3(256), 0, st, p, perm, nblk, out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
-// n16: buffer size in 16-byte units; unroll in {4, 8, 16}.  Returns a hipError_t.
+// n16: buffer size in 16-byte units; unroll in {4, 8, 16}; nontemporal: 0 plain
+// loads, 1 loads with the non-temporal hint.  Returns a hipError_t.
 extern "C" int kvcp_seq_read(const void* p, int64_t n16, void* out, int grid, int unroll,
-                             void* stream) {
+                             int nontemporal, void* stream) {
     if (!p || !out || n16 < 0 || grid < 1) return (int)hipErrorInvalidValue;
+    const uint4* b = (const uint4*)p;
     hipStream_t st = (hipStream_t)stream;
-    switch (unroll) {
-        case 4: hipLaunchKernelGGL(seq_read<4>, dim3(grid), dim3(256), 0, st, (const uint4*)p, n16, (uint32_t*)out); break;
-        case 8: hipLaunchKernelGGL(seq_read<8>, dim3(grid), dim3(256), 0, st, (const uint4*)p, n16, (uint32_t*)out); break;
-        case 16: hipLaunchKernelGGL(seq_read<16>, dim3(grid), dim3(256), 0, st, (const uint4*)p, n16, (uint32_t*)out); break;
-        default: return (int)hipErrorInvalidValue;
-    }
-    return (int)hipGetLastError();
+    return (int)(nontemporal ? launch_seq<true>(b, n16, (uint32_t*)out, grid, unroll, st)
+                             : launch_seq<false>(b, n16, (uint32_t*)out, grid, unroll, st));
 }
 
 // p holds nblk 4 KiB blocks; perm is a permutation of 0 .. nblk-1 (device,
-// int32); unroll in {2, 4, 8}.  Returns a hipError_t.
+// int32); unroll in {2, 4, 8}; nontemporal as above.  Returns a hipError_t.
 extern "C" int kvcp_block_read(const void* p, const void* perm, int64_t nblk, void* out, int grid,
-                               int unroll, void* stream) {
+                               int unroll, int nontemporal, void* stream) {
     if (!p || !perm || !out || nblk < 0 || grid < 1) return (int)hipErrorInvalidValue;
-    hipStream_t st = (hipStream_t)stream;
     const uint4* b = (const uint4*)p;
     const int32_t* pm = (const int32_t*)perm;
-    switch (unroll) {
-        case 2: hipLaunchKernelGGL(block_read<2>, dim3(grid), dim3(256), 0, st, b, pm, nblk, (uint32_t*)out); break;
-        case 4: hipLaunchKernelGGL(block_read<4>, dim3(grid), dim3(256), 0, st, b, pm, nblk, (uint32_t*)out); break;
-        case 8: hipLaunchKernelGGL(block_read<8>, dim3(grid), dim3(256), 0, st, b, pm, nblk, (uint32_t*)out); break;
-        default: return (int)hipErrorInvalidValue;
-    }
-    return (int)hipGetLastError();
+    hipStream_t st = (hipStream_t)stream;
+    return (int)(nontemporal ? launch_block<true>(b, pm, nblk, (uint32_t*)out, grid, unroll, st)
+                             : launch_block<false>(b, pm, nblk, (uint32_t*)out, grid, unroll, st));
 }

@@ -359,17 +359,19 @@ def cpu_baseline(wl, steps, every, min_seconds=10.0, max_passes=8):
 def stream_read_ceiling(gib=4):
     """Practical HBM read ceiling: best GB/s of plain streaming-read kernels
     (libkvc_probe.so) over a small sweep of launch shapes, sequential and in
-    random 4 KiB blocks (the decode kernel's pattern).  None without the probe
-    library."""
+    random 4 KiB blocks (the decode kernel's pattern), each with plain loads
+    and with non-temporal loads; the ceiling is the best of the block reads.
+    None without the probe library."""
     import ctypes
     path = os.path.join(ROOT, "batching_kv_append_amd", "libkvc_probe.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
     lib.kvcp_seq_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                  ctypes.c_int, ctypes.c_void_p]
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.kvcp_block_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
     nbytes = gib << 30
     buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
     nblk = nbytes // 4096
@@ -393,14 +395,21 @@ def stream_read_ceiling(gib=4):
             out_gbps = max(out_gbps, nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9)
         return out_gbps
 
-    seq = best(lambda o, gr, u: lib.kvcp_seq_read(buf.data_ptr(), nbytes // 16, o.data_ptr(), gr,
-                                                  u, st),
-               [(2048, 8), (4096, 8), (4096, 16), (8192, 8)])
-    blk = best(lambda o, gr, u: lib.kvcp_block_read(buf.data_ptr(), perm.data_ptr(), nblk,
-                                                    o.data_ptr(), gr, u, st),
-               [(2048, 4), (4096, 4), (2048, 8), (4096, 2)])
+    res = {}
+    for nt, tag in ((0, ""), (1, "_nontemporal")):
+        res["sequential" + tag + "_gbps"] = best(
+            lambda o, gr, u: lib.kvcp_seq_read(buf.data_ptr(), nbytes // 16, o.data_ptr(), gr, u,
+                                               nt, st),
+            [(2048, 8), (4096, 8), (4096, 16), (8192, 8)])
+        res["random_4kib_blocks" + tag + "_gbps"] = best(
+            lambda o, gr, u: lib.kvcp_block_read(buf.data_ptr(), perm.data_ptr(), nblk,
+                                                 o.data_ptr(), gr, u, nt, st),
+            [(1024, 4), (2048, 4), (4096, 4), (2048, 8), (4096, 2)])
     del buf, perm
-    return {"sequential_gbps": seq, "random_4kib_blocks_gbps": blk, "buffer_gib": gib}
+    res["ceiling_gbps"] = max(res["random_4kib_blocks_gbps"],
+                              res["random_4kib_blocks_nontemporal_gbps"])
+    res["buffer_gib"] = gib
+    return res
 
 
 def host_alloc_cost(wl, steps, reps=20):
@@ -594,7 +603,7 @@ def main():
                   "with_merge_gbps": alg["decode_kv_bytes"] / ((dec_us + merge_us) * 1e-6) / 1e9,
                   "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
                   "frac_random_4kib_read_ceiling":
-                      gbps / ceiling["random_4kib_blocks_gbps"] if ceiling else None}
+                      gbps / ceiling["ceiling_gbps"] if ceiling else None}
     prefill = None
     if alg["prefill_flops"]:
         tf = alg["prefill_flops"] / (pre_us * 1e-6) / 1e12

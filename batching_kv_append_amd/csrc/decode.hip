@@ -493,12 +493,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
 // heads that share a kv head are stacked as columns (up to 16):
 //   S^T[token][head] = K[token][:] . Q^T[:][head]      v_mfma_f32_16x16x32_bf16
 //   O^T[dim][head]  += V^T[dim][token] . P^T[token][head]
-// K goes straight from global memory into the A operand (lane l owns token
-// l%16 of a 16-token block and 8 dims of each 32-dim step); the score
-// registers of a lane (head l%16, tokens 4g..4g+3 of each block, g = l/16)
-// are already the B operand of the second product for a 32-token step, with
-// the key order {4g..4g+3, 16+4g..16+4g+3}; V is transposed through a
-// per-wave 8 KiB LDS tile in that same order.  The four lanes of a head
+// K rows are loaded whole and rearranged through a per-wave 8 KiB LDS tile
+// into the A operand (lane l owns token l%16 of a 16-token block and 8 dims
+// of each 32-dim step); the score registers of a lane (head l%16, tokens
+// 4g..4g+3 of each block, g = l/16) are already the B operand of the second
+// product for a 32-token step, with the key order {4g..4g+3, 16+4g..16+4g+3};
+// V is transposed through the same tile in that same order.  The four lanes of a head
 // column share one running maximum (two lane exchanges per step), so the
 // weights summed by one matrix instruction share one scale.  The VALU work per
 // 32-token step is about 80 instructions, far under the bytes' HBM time.
@@ -632,30 +632,33 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         }
     };
 
+    // K and V are streamed with the non-temporal hint: each line is used
+    // once, and the hint keeps it from displacing other data in L2 (V alone
+    // gave 7 % more bandwidth, K as well 4 % more on the GQA batch).  The
+    // hint only pays when one load instruction covers whole 128-byte lines:
+    // loading K straight in the MFMA operand layout covers half of each line
+    // per instruction, and the hint made the other half miss, so K rows are
+    // loaded whole and rearranged through LDS.
+    auto v_stream = [&](const uint4* ptr) -> uint4 {
+        return __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(ptr)));
+    };
     for (int tc = t0; tc < t1; tc += STEP) {
-        // ---- K: two 16-token blocks x four 32-dim steps -------------------
-        uint4 kb[2][4];
+        // ---- K: 32 rows, four per load, each row whole (16 lanes x 16 B) --
+        // Lane (g, col) of load j reads chunk col of row 4j + g; the rows then
+        // pass through the wave's LDS tile into the MFMA operand layout.
+        uint4 kst[8];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int t = min(tc + 16 * b + col, t1 - 1);
-            int64_t blk = block_of(t, min(tc + 16 * b, t1 - 1));
+        for (int j = 0; j < 8; ++j) {
+            const int t = min(tc + 4 * j + g, t1 - 1);
+            int64_t blk = block_of(t, min(tc + 16 * (j >> 2), t1 - 1));
             if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
-            const uint4* kp = P.k_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + g;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kb[b][ks] = kp[ks * 4];
+            kst[j] = v_stream(P.k_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col);
         }
         // ---- V: token groups g and g+4 (4 tokens each) x chunk col --------
-        // Each V load instruction reads whole 256-byte rows, so V is streamed
-        // with the non-temporal hint: the lines are used once and do not
-        // displace other data in L2 (about 7 % more bandwidth).  Both branches
-        // load through the same helper, since merging a non-temporal load with
-        // a plain one drops the hint.  K stays on plain loads: one K load
-        // instruction covers half of each 128-byte line, and the hint made the
-        // second half miss.
-        auto v_stream = [&](const uint4* ptr) -> uint4 {
-            return __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4_t*>(ptr)));
-        };
+        // Each load instruction reads four whole 256-byte rows.  Both
+        // branches load through the same helper, since merging a
+        // non-temporal load with a plain one drops the hint.
         uint4 vb[2][4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -673,6 +676,24 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
                     vb[hh][j] = v_stream(vp + (min(tc + 4 * tg + j, t1 - 1) - t) * CPR);
             }
         }
+
+        // K rows into this wave's tile ([row][chunk ^ row % 16]), then the
+        // A operands: lane (g, col) of block b, step ks takes chunk 4 ks + g
+        // of row 16 b + col.  The V^T stores below reuse the tile after these
+        // reads (same wave, in order).
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 4 * j + g;
+            vt[r * 16 + (col ^ (r & 15))] = kst[j];
+        }
+        uint4 kb[2][4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int r = 16 * b + col;
+                kb[b][ks] = vt[r * 16 + ((4 * ks + g) ^ (r & 15))];
+            }
 
         // ---- S^T for the two blocks, per head group ---------------------------
         f32x4_t sc[NG][2];

@@ -464,11 +464,12 @@ def source_digest(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summaries in profiles/,
-    or None when none was taken on the kernel's current code."""
+    or None when none was taken on this workload with the kernel's current
+    code."""
     import glob
-    key = f"traffic {kernel} src_sha256_16={source_digest(kernel)} "
+    key = f"traffic {kernel} workload={workload} src_sha256_16={source_digest(kernel)} "
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as fh:
             for line in fh:
@@ -618,14 +619,14 @@ def main():
     if decode and (not prefill or dec_us >= pre_us):
         roofline = {"bound": "hbm", "kernel": "decode_mfma_kernel (split-K partials)",
                     "achieved": decode["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": decode["frac_hbm_peak"], "traffic": measured_traffic("decode_mfma_kernel"),
+                    "frac": decode["frac_hbm_peak"], "traffic": measured_traffic("decode_mfma_kernel", args.workload),
                     "algorithmic_bytes_per_launch": alg["decode_kv_bytes"] / launches,
                     "avg_launch_us": dec_us / launches}
     else:
         roofline = {"bound": "mfma", "kernel": "prefill_kernel (bf16 MFMA)",
                     "achieved": prefill["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": prefill["frac_mfma_peak"],
-                    "traffic": measured_traffic("prefill_kernel"),
+                    "traffic": measured_traffic("prefill_kernel", args.workload),
                     "algorithmic_flops_per_launch": alg["prefill_flops"] / launches,
                     "avg_launch_us": pre_us / launches}
 

@@ -11,6 +11,11 @@
 // Either reads with plain loads or with the non-temporal hint (data used once,
 // kept from displacing other lines in L2), which streams faster on gfx950.
 //
+//   kvcp_mfma_loop   back-to-back v_mfma_f32_32x32x16_bf16 on register operands
+//                    (four independent accumulators per wave): the practical
+//                    bf16 matrix rate the prefill kernel is compared with
+//                    beside the 2.5 PFLOP/s data-sheet figure
+//
 // Both reduce what they read into one word per thread so that the loads are
 // not removed; `out` needs grid * 256 uint32 words.
 #include <hip/hip_runtime.h>
@@ -74,6 +79,30 @@ __global__ __launch_bounds__(256) void block_read(const uint4* __restrict__ p,
 }
 
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void mfma_loop(float* __restrict__ out, int iters) {
+    const int lane = threadIdx.x & 63;
+    bf16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)((float)((lane + i) & 7) * 0.125f);
+        b[i] = (__bf16)((float)((lane * 3 + i) & 7) * 0.125f);
+    }
+    f32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 template <bool NT>
 hipError_t launch_seq(const uint4* p, int64_t n16, uint32_t* out, int grid, int unroll, hipStream_t st) {
     switch (unroll) {
@@ -120,4 +149,13 @@ extern "C" int kvcp_block_read(const void* p, const void* perm, int64_t nblk, vo
     hipStream_t st = (hipStream_t)stream;
     return (int)(nontemporal ? launch_block<true>(b, pm, nblk, (uint32_t*)out, grid, unroll, st)
                              : launch_block<false>(b, pm, nblk, (uint32_t*)out, grid, unroll, st));
+}
+
+// grid workgroups of 4 waves, each wave iters x 4 matrix instructions of
+// 32 x 32 x 16 (2 x 32 x 32 x 16 flops each); out needs grid * 256 floats.
+// Returns a hipError_t.
+extern "C" int kvcp_mfma_loop(void* out, int grid, int iters, void* stream) {
+    if (!out || grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_loop, dim3(grid), dim3(256), 0, (hipStream_t)stream, (float*)out, iters);
+    return (int)hipGetLastError();
 }

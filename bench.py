@@ -412,6 +412,35 @@ def stream_read_ceiling(gib=4):
     return res
 
 
+def mfma_ceiling():
+    """Practical bf16 matrix rate: back-to-back v_mfma_f32_32x32x16_bf16 on
+    register operands with 2 or 3 waves per SIMD on every CU (libkvc_probe.so),
+    best TFLOP/s.  None without the probe library."""
+    import ctypes
+    path = os.path.join(ROOT, "batching_kv_append_amd", "libkvc_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.kvcp_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters, best = 8192, 0.0
+    for per_cu in (2, 3):
+        grid = cus * per_cu
+        out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+        assert lib.kvcp_mfma_loop(out.data_ptr(), grid, iters, st) == 0
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(3):
+            assert lib.kvcp_mfma_loop(out.data_ptr(), grid, iters, st) == 0
+        e.record(stream)
+        torch.cuda.synchronize()
+        flops = 3 * grid * 4 * iters * 4 * 2 * 32 * 32 * 16
+        best = max(best, flops / (s.elapsed_time(e) * 1e-3) / 1e12)
+    return {"bf16_32x32x16_tflops": best}
+
+
 def host_alloc_cost(wl, steps, reps=20):
     """Host block allocation for the step (just-in-time table growth of every
     sequence by its new tokens, one kvc_extend_tables call for all rows),
@@ -596,6 +625,7 @@ def main():
     merge_us = per_step_us["merge"]
     pre_us = per_step_us["prefill"]
     ceiling = stream_read_ceiling()
+    mfma_ceil = mfma_ceiling()
     decode = None
     if alg["decode_kv_bytes"]:
         gbps = alg["decode_kv_bytes"] / (dec_us * 1e-6) / 1e9
@@ -610,7 +640,9 @@ def main():
         tf = alg["prefill_flops"] / (pre_us * 1e-6) / 1e12
         prefill = {"flops_per_step": alg["prefill_flops"], "visible_pairs_per_head":
                    alg["prefill_pairs"], "kernel_us": pre_us, "tflops": tf,
-                   "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+                   "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                   "frac_measured_mfma_ceiling":
+                       tf / mfma_ceil["bf16_32x32x16_tflops"] if mfma_ceil else None}
         if decode:
             prefill["note"] = ("runs on the side stream under the decode: kernel_us is its "
                                "window beside the decode, not its own speed")
@@ -653,6 +685,8 @@ def main():
         "host_alloc_us_per_step": host_alloc_cost(wl, steps),
         # measured streaming-read ceiling beside the data-sheet 8 TB/s
         "stream_read_ceiling": ceiling,
+        # measured matrix-core rate beside the data-sheet 2.5 PFLOP/s
+        "mfma_ceiling": mfma_ceil,
         "input_gen_s": gen_s,
     }
     if not args.no_cpu_baseline:

@@ -41,6 +41,7 @@ def test_measurement_probe_library_loads():
     assert os.path.exists(path), "build with batching_kv_append_amd/build.py"
     lib = ctypes.CDLL(path)
     assert hasattr(lib, "kvcp_seq_read") and hasattr(lib, "kvcp_block_read")
+    assert hasattr(lib, "kvcp_mfma_loop")
 
 
 def test_status_strings(kvc):

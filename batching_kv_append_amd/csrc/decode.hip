@@ -6,11 +6,14 @@
 // decode stage is limited by memory access; clvsit.github.io AWS SageMaker
 // page: every step moves the parameters and the cache into the compute
 // units).  The kernels therefore aim at HBM bandwidth:
-//   * a sequence's context is cut into fixed partitions of DECODE_PART tokens
-//     (split-K), so even a short batch of long contexts yields thousands of
-//     independent pieces of work; the partial softmax states are combined by
-//     an exact log-sum-exp merge (an exact regrouping of the row-wise softmax
-//     of the "Attention" section of the continuous-batching article);
+//   * a sequence's context is cut into pieces of at most DECODE_PART tokens
+//     (split-K), a cut that depends only on its own length, so even a short
+//     batch of long contexts yields thousands of independent pieces of work;
+//     the partial softmax states are combined by an exact log-sum-exp merge
+//     (an exact regrouping of the row-wise softmax of the "Attention" section
+//     of the continuous-batching article);
+//   * K and V are streamed with non-temporal loads whose instructions each
+//     cover whole 128-byte lines;
 //   * the GW query heads that share a kv head (GQA, e2hang/Notes "MQA与GQA")
 //     are served from one read of K/V;
 //   * head_dim 128 (decode_mfma_kernel): a sequence is cut into
@@ -21,9 +24,10 @@
 //     item;
 //   * head_dim 16 (decode_kernel): one wave per partition, 16 lanes per
 //     token row, dot products reduced with DPP row operations.
-// The planning kernel lists the work items on the device, so the host needs
-// no copy of the lengths, and the hardware dispatcher hands the next
-// workgroup to whichever compute unit frees up first.
+// The planning kernel lists the work items on the device, longest pieces
+// first, so the host needs no copy of the lengths, and the hardware
+// dispatcher hands the next workgroup to whichever compute unit frees up
+// first.
 #include <hip/hip_runtime.h>
 
 #include "kvc_launch.h"

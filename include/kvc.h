@@ -272,7 +272,10 @@ size_t kvc_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
  *      Rows with q_len_s == 1 take the split-K decode path, rows of longer
  *      chunks the MFMA prefill path; both compute the same function.
  * max_q_len / max_context_len are host-side upper bounds (no device readback);
- * they size the work lists, so they must not be exceeded.  scale must be
+ * they size the work lists, so they must not be exceeded.  total_q must equal
+ * cu_seqlens_q[num_seqs]; together with num_seqs and max_q_len it also picks
+ * the launches: when total_q > (num_seqs - 1) * max_q_len + 1 no row can be a
+ * decode row, and the decode and merge launches are skipped.  scale must be
  * finite.  workspace: device memory of at least
  * kvc_workspace_size(num_seqs, total_q, max_q_len, max_context_len, ...) bytes,
  * 256-byte aligned, owned by the caller; it may be reused across calls that

@@ -616,6 +616,42 @@ def main():
     phase_ms, ncalls = kvc.kvc_profile_end()
     assert ncalls == args.steps * len(calls), (ncalls, args.steps * len(calls))
     per_step_us = {k: v * 1e3 / args.steps for k, v in phase_ms.items()}
+    # Cold caches: each step after a read of a 1 GiB scratch buffer (more than
+    # the L2s and the 256 MB last-level cache hold; read only, so no dirty
+    # lines are left to be written back during the step), timed by events
+    # around the step alone, as when other layers run between two steps of
+    # one layer.  Everything is queued before one final wait, so the GPU runs
+    # scratch pass, event, step, event, ... and no host launch latency is
+    # timed.
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    probe = None
+    probe_path = os.path.join(ROOT, "batching_kv_append_amd", "libkvc_probe.so")
+    if os.path.exists(probe_path):
+        import ctypes
+        probe = ctypes.CDLL(probe_path)
+        probe.kvcp_seq_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+
+    def read_scratch():
+        if probe is None:
+            scratch.sum()
+        else:
+            assert probe.kvcp_seq_read(scratch.data_ptr(), scratch.numel() // 4, sink.data_ptr(),
+                                       4096, 8, 0, ctypes.c_void_p(stream.cuda_stream)) == 0
+
+    torch.cuda.synchronize()
+    cold_ev = []
+    for _ in range(min(args.steps, 10)):
+        read_scratch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        one_step()
+        e1.record(stream)
+        cold_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    cold_ms = [a.elapsed_time(b) for a, b in cold_ev]
+    del scratch, sink
 
     alg = algorithmic(wl, steps)
     ms_per_step = elapsed * 1e3 / args.steps
@@ -667,6 +703,7 @@ def main():
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "ms_per_step_kernel_events_pass": elapsed_events * 1e3 / args.steps,
+        "ms_per_step_cold_cache": float(np.median(cold_ms)),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the pages' workloads)",
         "config": {"workload": desc, "name": args.workload, "calls_per_step": len(calls),

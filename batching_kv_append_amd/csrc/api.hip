@@ -12,7 +12,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
+#include <memory>
 #include <mutex>
+#include <utility>
 #include <algorithm>
 #include <vector>
 
@@ -84,6 +87,13 @@ int hip_fail(hipError_t e, const char* fn) {
     return kvc_fail(KVC_ERR_HIP, msg);
 }
 
+// "<fn>: <detail>" in a thread-local buffer (kvc_fail copies it at once).
+const char* fmt_msg(const char* fn, const char* detail) {
+    thread_local char buf[256];
+    std::snprintf(buf, sizeof buf, "%s: %s", fn, detail);
+    return buf;
+}
+
 // KVC_DEBUG=1: copy lengths and table back and check them on the host.
 int debug_check(const int32_t* cu_d, const int32_t* ctx_d, const int32_t* table_d, int32_t num_seqs,
                 int32_t total_q, int32_t max_q_len, int32_t max_context_len, int32_t max_blocks,
@@ -116,7 +126,9 @@ int debug_check(const int32_t* cu_d, const int32_t* ctx_d, const int32_t* table_
 
 // Optional per-kernel timing: a start and an end HIP event around each kernel
 // of kvc_paged_attention_varlen, recorded on the stream that kernel runs on
-// (kvc_profile_begin/end).
+// (kvc_profile_begin/end).  g_prof_on is read without the lock; a call takes
+// g_prof_mu only while timing is on, so untimed calls from several threads
+// never wait for each other here.
 struct Profiler {
     bool on = false;
     int32_t max_calls = 0, calls = 0;
@@ -125,7 +137,9 @@ struct Profiler {
 };
 Profiler g_prof;
 std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
 
+// Caller holds g_prof_mu.
 void prof_mark(int phase, bool end, hipStream_t st) {
     if (!g_prof.on || g_prof.calls >= g_prof.max_calls) return;
     const size_t base = (size_t)g_prof.calls * KVC_PROF_PHASES + phase;
@@ -135,33 +149,47 @@ void prof_mark(int phase, bool end, hipStream_t st) {
         g_prof.used[base] = 1;
 }
 
-// Side stream per device for the prefill kernel, so the matrix-bound prefill
-// overlaps the memory-bound decode.  The call forks to it with an event after
-// the append and joins it with another before returning, so the caller's
-// stream still sees one ordered step.  Created once per device (default
-// priority, non-blocking); a mutex keeps the fork/join event pair of
-// concurrent callers apart.
+// Side streams for the prefill kernel, so the matrix-bound prefill overlaps
+// the memory-bound decode.  Each caller stream gets its own side stream and
+// fork/join event pair (per device, created on first use, default priority,
+// non-blocking), so steps issued on different caller streams are not chained
+// through one shared side stream.  A call forks to the side stream with an
+// event after the append and joins it back with another before returning,
+// so the caller's stream still sees one ordered step.  The per-entry mutex
+// keeps the event pair of two threads using the same caller stream apart.
+// Past kMaxSides caller streams on a device, new callers share an existing
+// entry (chosen by the stream handle); that only orders their prefills.
 struct SideStream {
     std::mutex mu;
-    bool ready = false;
     hipStream_t stream = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
 };
-SideStream g_side[64];
+constexpr size_t kMaxSides = 64;
+struct DeviceSides {
+    std::mutex mu;
+    std::vector<std::pair<hipStream_t, std::unique_ptr<SideStream>>> by_caller;
+};
+DeviceSides g_sides[64];
 
-SideStream* side_stream() {
+SideStream* side_stream(hipStream_t caller) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    SideStream& ss = g_side[dev];
-    std::lock_guard<std::mutex> lk(ss.mu);
-    if (!ss.ready) {
-        if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-            return nullptr;
-        ss.ready = true;
+    DeviceSides& ds = g_sides[dev];
+    std::lock_guard<std::mutex> lk(ds.mu);
+    for (auto& e : ds.by_caller)
+        if (e.first == caller) return e.second.get();
+    if (ds.by_caller.size() >= kMaxSides)
+        return ds.by_caller[((uintptr_t)caller >> 4) % ds.by_caller.size()].second.get();
+    auto ss = std::make_unique<SideStream>();
+    if (hipStreamCreateWithFlags(&ss->stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) != hipSuccess) {
+        if (ss->fork) (void)hipEventDestroy(ss->fork);
+        (void)hipStreamDestroy(ss->stream);
+        return nullptr;
     }
-    return &ss;
+    ds.by_caller.emplace_back(caller, std::move(ss));
+    return ds.by_caller.back().second.get();
 }
 
 bool overlap_enabled() {
@@ -175,6 +203,7 @@ extern "C" int kvc_profile_begin(int32_t max_calls) {
     if (max_calls < 1 || max_calls > 100000)
         return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_profile_begin: max_calls out of range");
     std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on.store(false, std::memory_order_release);
     for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
     g_prof = Profiler{};
     g_prof.ev.resize((size_t)max_calls * KVC_PROF_PHASES * 2);
@@ -185,12 +214,14 @@ extern "C" int kvc_profile_begin(int32_t max_calls) {
     }
     g_prof.max_calls = max_calls;
     g_prof.on = true;
+    g_prof_on.store(true, std::memory_order_release);
     return KVC_OK;
 }
 
 extern "C" int kvc_profile_end(double* ms_sum, int32_t* calls) {
     if (!ms_sum || !calls) return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_profile_end: NULL pointer");
     std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on.store(false, std::memory_order_release);
     for (int p = 0; p < KVC_PROF_PHASES; ++p) ms_sum[p] = 0.0;
     *calls = 0;
     for (int32_t c = 0; c < g_prof.calls; ++c) {
@@ -299,6 +330,73 @@ extern "C" int kvc_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
     return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
 }
 
+namespace {
+
+// Enqueue one planned step: plan + append, then the prefill (on the caller
+// stream's side stream when the step also has decode rows) beside the decode
+// and merge on the caller's stream.  Once the side stream has been forked,
+// the join is recorded on every path, launch failures included, and the
+// caller's stream waits on it after the decode and merge launches; if the
+// join cannot be recorded or waited on, the host waits for the side stream
+// instead, so nothing queued there can outlive the call unordered.
+int run_step(const kvc::StepArgs& a, bool has_decode, bool overlap, const char* fn) {
+    const hipStream_t st = a.stream;
+    const int32_t max_q_len = a.max_q_len;
+    const bool profiling = g_prof_on.load(std::memory_order_acquire);
+    std::unique_lock<std::mutex> prof_lk(g_prof_mu, std::defer_lock);
+    if (profiling) prof_lk.lock();
+    auto mark = [&](int phase, bool end, hipStream_t s) {
+        if (profiling) prof_mark(phase, end, s);
+    };
+    // planning and append share one launch (counted under "plan")
+    mark(KVC_PROF_PLAN, false, st);
+    hipError_t e = kvc::launch_prep(a, a.k_new != nullptr);
+    mark(KVC_PROF_PLAN, true, st);
+    // The prefill kernel (rows of chunks with >= 2 new tokens) runs on the side
+    // stream when there is one, concurrently with decode and merge.
+    SideStream* ss =
+        (max_q_len >= 2 && has_decode && overlap) ? side_stream(st) : nullptr;
+    std::unique_lock<std::mutex> side_lk;
+    if (ss) side_lk = std::unique_lock<std::mutex>(ss->mu);
+    bool forked = false;
+    if (e == hipSuccess && max_q_len >= 2) {
+        kvc::StepArgs ap = a;
+        if (ss) {
+            e = hipEventRecord(ss->fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+            forked = e == hipSuccess;
+            ap.stream = ss->stream;
+        }
+        mark(KVC_PROF_PREFILL, false, ap.stream);
+        if (e == hipSuccess) e = kvc::launch_prefill(ap);
+        mark(KVC_PROF_PREFILL, true, ap.stream);
+    }
+    // the join is recorded even after a failed prefill launch
+    hipError_t ej = forked ? hipEventRecord(ss->join, ss->stream) : hipSuccess;
+    if (has_decode) {
+        mark(KVC_PROF_DECODE, false, st);
+        if (e == hipSuccess) e = kvc::launch_decode(a);
+        mark(KVC_PROF_DECODE, true, st);
+        mark(KVC_PROF_MERGE, false, st);
+        if (e == hipSuccess) e = kvc::launch_merge(a);
+        mark(KVC_PROF_MERGE, true, st);
+    }
+    if (forked) {
+        // the caller's stream never runs ahead of work queued on the side
+        // stream: it waits on this call's join, or the host waits for the
+        // side stream when the join could not be recorded or waited on
+        if (ej == hipSuccess) ej = hipStreamWaitEvent(st, ss->join, 0);
+        if (ej != hipSuccess) {
+            (void)hipStreamSynchronize(ss->stream);
+            if (e == hipSuccess) e = ej;
+        }
+    }
+    if (profiling && g_prof.on && g_prof.calls < g_prof.max_calls) ++g_prof.calls;
+    return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
+}
+
+}  // namespace
+
 extern "C" size_t kvc_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                                      int32_t max_context_len, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
@@ -308,37 +406,42 @@ extern "C" size_t kvc_workspace_size(int32_t num_seqs, int32_t total_q, int32_t 
     return kvc::ws_layout(num_seqs, total_q, max_context_len, num_q_heads, num_kv_heads, head_dim).total;
 }
 
-extern "C" int kvc_paged_attention_varlen(
-    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-    int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
-    const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs, int32_t total_q,
-    int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
-    void* stream) {
-    const char* fn = "kvc_paged_attention_varlen";
+namespace kvc {
+
+// Checks and launches of one step (kvc_paged_attention_varlen and its
+// variants): `fn` names the entry point in error messages, `overlap` lets a
+// step with chunks and decode rows run its prefill on the side stream.
+int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
+                    const void* v_new, void* k_cache, void* v_cache, int64_t num_blocks,
+                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t total_q, int32_t max_q_len, int32_t max_context_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
+                    void* stream, bool overlap) {
     if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0)
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: negative size");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "negative size"));
     if (int rc = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, fn)) return rc;
     if (!std::isfinite(scale))
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: scale must be finite");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "scale must be finite"));
     if ((k_new == nullptr) != (v_new == nullptr))
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: k_new and v_new must both be set or both NULL");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "k_new and v_new must both be set or both NULL"));
     if (num_seqs == 0 || total_q == 0) return KVC_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !context_lens)
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: NULL pointer");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "NULL pointer"));
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
         (k_new && (!aligned16(k_new) || !aligned16(v_new))))
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: tensors must be 16-byte aligned");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "tensors must be 16-byte aligned"));
     if (num_blocks < 1 || max_blocks_per_seq < 1)
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: num_blocks and max_blocks_per_seq must be >= 1");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "num_blocks and max_blocks_per_seq must be >= 1"));
     if (max_q_len > total_q)
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: max_q_len > total_q");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "max_q_len > total_q"));
     if ((int64_t)max_context_len + max_q_len > INT32_MAX / 2)
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: lengths too large");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "lengths too large"));
     const WsLayout lay = kvc::ws_layout(num_seqs, total_q, max_context_len, num_q_heads,
                                         num_kv_heads, head_dim);
     if (lay.cap_dec > INT32_MAX / 64 || lay.cap_pre > INT32_MAX / 64)
-        return kvc_fail(KVC_ERR_INVALID_ARG, "kvc_paged_attention_varlen: step too large");
+        return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "step too large"));
     if (!workspace || workspace_bytes < lay.total) {
         char msg[256];
         std::snprintf(msg, sizeof msg, "%s: workspace of %zu bytes needed, %zu given", fn,
@@ -346,7 +449,7 @@ extern "C" int kvc_paged_attention_varlen(
         return kvc_fail(KVC_ERR_WORKSPACE, msg);
     }
     if (((uintptr_t)workspace & 255u) != 0)
-        return kvc_fail(KVC_ERR_WORKSPACE, "kvc_paged_attention_varlen: workspace must be 256-byte aligned");
+        return kvc_fail(KVC_ERR_WORKSPACE, fmt_msg(fn, "workspace must be 256-byte aligned"));
     hipStream_t st = (hipStream_t)stream;
     if (debug_mode()) {
         if (int rc = debug_check(cu_seqlens_q, context_lens, block_table, num_seqs, total_q,
@@ -390,45 +493,23 @@ extern "C" int kvc_paged_attention_varlen(
         max_q_len < 2 ||
         (int64_t)num_seqs * max_q_len - total_q >= (int64_t)max_q_len - 1;
 
-    std::unique_lock<std::mutex> prof_lk(g_prof_mu);
-    // planning and append share one launch (counted under "plan")
-    prof_mark(KVC_PROF_PLAN, false, st);
-    hipError_t e = kvc::launch_prep(a, k_new != nullptr);
-    prof_mark(KVC_PROF_PLAN, true, st);
-    // The prefill kernel (rows of chunks with >= 2 new tokens) runs on the side
-    // stream when there is one, concurrently with decode and merge.
-    SideStream* ss =
-        (max_q_len >= 2 && has_decode && overlap_enabled()) ? side_stream() : nullptr;
-    std::unique_lock<std::mutex> side_lk;
-    if (ss) side_lk = std::unique_lock<std::mutex>(ss->mu);
-    if (e == hipSuccess && max_q_len >= 2) {
-        kvc::StepArgs ap = a;
-        if (ss) {
-            e = hipEventRecord(ss->fork, st);
-            if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
-            ap.stream = ss->stream;
-        }
-        prof_mark(KVC_PROF_PREFILL, false, ap.stream);
-        if (e == hipSuccess) e = kvc::launch_prefill(ap);
-        prof_mark(KVC_PROF_PREFILL, true, ap.stream);
-        if (ss && e == hipSuccess) e = hipEventRecord(ss->join, ss->stream);
-    }
-    if (has_decode) {
-        prof_mark(KVC_PROF_DECODE, false, st);
-        if (e == hipSuccess) e = kvc::launch_decode(a);
-        prof_mark(KVC_PROF_DECODE, true, st);
-        prof_mark(KVC_PROF_MERGE, false, st);
-        if (e == hipSuccess) e = kvc::launch_merge(a);
-        prof_mark(KVC_PROF_MERGE, true, st);
-    }
-    if (ss) {
-        // join even after a failed launch, so the caller's stream never runs
-        // ahead of work already queued on the side stream
-        hipError_t ej = hipStreamWaitEvent(st, ss->join, 0);
-        if (e == hipSuccess) e = ej;
-    }
-    if (g_prof.on && g_prof.calls < g_prof.max_calls) ++g_prof.calls;
-    return e == hipSuccess ? KVC_OK : hip_fail(e, fn);
+    return run_step(a, has_decode, overlap, fn);
+}
+
+}  // namespace kvc
+
+extern "C" int kvc_paged_attention_varlen(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+    const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs, int32_t total_q,
+    int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    return kvc::paged_attention("kvc_paged_attention_varlen", out, q, k_new, v_new, k_cache,
+                                v_cache, num_blocks, block_table, max_blocks_per_seq,
+                                cu_seqlens_q, context_lens, num_seqs, total_q, max_q_len,
+                                max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                                scale, workspace, workspace_bytes, stream, overlap_enabled());
 }
 
 extern "C" int kvc_workspace_flags(const void* workspace, void* stream, int32_t* flags) {

@@ -773,14 +773,16 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             }
             float p[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(fmaf(v8[r], mc, -m[ng]));
-                lsum[ng] += p[r];
-            }
+            for (int r = 0; r < 8; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(v8[r], mc, -m[ng]));
             pb[ng].x = pack_bf16x2(p[0], p[1]);
             pb[ng].y = pack_bf16x2(p[2], p[3]);
             pb[ng].z = pack_bf16x2(p[4], p[5]);
             pb[ng].w = pack_bf16x2(p[6], p[7]);
+            // the denominator sums the bf16 weights the P.V product multiplies
+            lsum[ng] = sum_bf16x2(pb[ng].x, lsum[ng]);
+            lsum[ng] = sum_bf16x2(pb[ng].y, lsum[ng]);
+            lsum[ng] = sum_bf16x2(pb[ng].z, lsum[ng]);
+            lsum[ng] = sum_bf16x2(pb[ng].w, lsum[ng]);
         }
 
         // ---- O^T += V^T P^T (one V^T fragment for all head groups) ------------

@@ -93,6 +93,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 with (1, 1)): the
+// softmax denominators sum the same bf16-rounded weights that the P.V matrix
+// products multiply.
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
 // Sum over groups of LANES consecutive lanes (LANES in {2, 4, 8, 16}) with DPP
 // row operations; every lane of a group ends with the group's sum.
 template <int LANES>

@@ -92,13 +92,6 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 with (1, 1)).
-__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
-}
-
 // XOR swizzle of the 16-byte chunks of V row `row` (a key of the tile):
 // 0, 6, 10, 12 for row % 4 = 0..3, and 8 more when row % 16 >= 8.  A
 // transposing read takes 4 consecutive rows x 2 (16 lanes) or 4 (32 lanes)

@@ -48,12 +48,18 @@
  *   Heads     Query head h reads kv head h / (num_q_heads / num_kv_heads).
  *   Streams   `stream` is a hipStream_t (NULL = the null stream).  Device
  *             work is enqueued asynchronously, in stream order.  When a step
- *             has prefill chunks, kvc_paged_attention_varlen runs the prefill
- *             kernel on one internal side stream per device (created on first
- *             use, default priority), forked from `stream` after the append
- *             and joined back before the call returns, so it overlaps the
- *             decode kernels; to the caller the step is still one ordered
- *             piece of `stream`.  KVC_SERIAL=1 keeps every kernel on `stream`.
+ *             has both prefill chunks and decode rows,
+ *             kvc_paged_attention_varlen runs the prefill kernel on an
+ *             internal side stream that belongs to `stream` (one per caller
+ *             stream and device, created on first use, default priority),
+ *             forked from `stream` after the append and joined back before
+ *             the call returns, so it overlaps the decode kernels; to the
+ *             caller the step is still one ordered piece of `stream`: work
+ *             the caller enqueues on `stream` afterwards (a copy of `out`, the
+ *             next step reusing the workspace) starts after the whole step.
+ *             If the join cannot be enqueued, the call waits on the host for
+ *             the side stream before returning the error.  KVC_SERIAL=1
+ *             keeps every kernel on `stream`.
  *   Errors    Every entry point returns a kvc_status.  Arguments are checked
  *             before anything is enqueued, so a call that returns an error
  *             has had no effect.  Values inside device arrays (table entries,
@@ -68,7 +74,11 @@
  *             num_q_heads % num_kv_heads == 0 with ratio G = 1, 2 or any
  *             multiple of 4 (MHA, GQA, MQA).  Others return
  *             KVC_ERR_UNSUPPORTED.
- *   Threads   Entry points are reentrant; an allocator object is not
+ *   Threads   Entry points are reentrant, and calls on different streams
+ *             from different host threads do not wait for each other: only
+ *             two threads calling on the same stream share its side stream's
+ *             event pair (under a mutex), and per-kernel timing, while on,
+ *             takes a lock.  An allocator or scheduler object is not
  *             thread-safe (one owner at a time).
  */
 #ifndef KVC_H

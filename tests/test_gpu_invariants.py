@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import run_steps
+from gpu_util import compare, oracle_run, run_steps
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +123,62 @@ def test_no_poison_leaks(kvc):
     gv = W.bits_to_f32(g)
     assert np.isfinite(gv).all()
     assert np.abs(gv).max() < 100.0
+
+
+DEC_N = [1, 2, 15, 16, 63, 64, 65, 300, 1023, 1024, 1500, 4097]
+
+
+def test_decode_equals_last_prefill_row(kvc, orc):
+    """Row n of a prefill over tokens 0..n (the chunk that ends at token n)
+    and the decode row of token n over n cached tokens are the same function
+    (news.myit.tw article, "KV cache": with the cache, the new token's
+    attention is the last row of the full computation).  On the GPU they run
+    through different kernels (prefill: 32x32x16 products over 64-key tiles;
+    decode: 16x16x32 products over split-K partitions), and both round the
+    softmax weights to bf16 for the P.V product and sum the same rounded
+    weights in the denominator.  Bound: the two results may sit on either side
+    of a bf16 rounding of the output (one ulp of the value) and differ before
+    rounding by the weight rounding (relative 2^-9 per weight, which with few
+    keys moves the output by up to about |v_i - v_j| / 4 * 2^-8); hence
+    |decode - prefill| <= 2^-7 |oracle| + 4e-3 per element and a mean under
+    3e-4, both well inside the 2e-2 / 2e-3 oracle tolerance."""
+    hq, hkv, a, bs = 8, 2, 128, 16
+    wd = W.make_step_workload("dec", [(n, 1) for n in DEC_N], num_q_heads=hq, num_kv_heads=hkv,
+                              head_dim=a, block_size=bs, seed=41)
+    (gd,), kc, vc = run_steps(kvc, wd)
+    (rd,), _, _ = oracle_run(orc, wd)
+    compare(gd, rd, what="decode rows")
+    st = wd.steps[0]
+    # the chunk: the last m tokens of each sequence (its K/V already in the pool)
+    ms = [min(64, n + 1) for n in DEC_N]
+    extra_q = W._normal_bf16(sum(ms) * hq * a, 42, "q").reshape(sum(ms), hq, a)
+    q, kn, vn, last = [], [], [], []
+    o = 0
+    for s, (n, m) in enumerate(zip(DEC_N, ms)):
+        for p in range(n + 1 - m, n + 1):
+            if p == n:
+                kn.append(st.k_new[s])
+                vn.append(st.v_new[s])
+            else:
+                blk = st.block_table[s, p // bs]
+                kn.append(wd.k_pool[blk, :, p % bs, :])
+                vn.append(wd.v_pool[blk, :, p % bs, :])
+        q.append(extra_q[o:o + m - 1])
+        q.append(st.q[s:s + 1])
+        o += m
+        last.append(o - 1)
+    cu = np.concatenate([[0], np.cumsum(ms)]).astype(np.int32)
+    pre = W.Step(q=np.concatenate(q), k_new=np.stack(kn), v_new=np.stack(vn), cu_seqlens_q=cu,
+                 context_lens=np.array([n + 1 - m for n, m in zip(DEC_N, ms)], np.int32),
+                 block_table=st.block_table)
+    # the chunk rewrites the same K/V into the pool the decode call left
+    (gp,), _, _ = run_steps(kvc, wd, [pre], k_cache=kc, v_cache=vc)
+    gl = gp[last]
+    dv = W.bits_to_f32(gd).astype(np.float64)
+    pv = W.bits_to_f32(gl).astype(np.float64)
+    diff = np.abs(dv - pv)
+    bound = 2.0 ** -7 * np.abs(rd) + 4e-3
+    print(f"decode vs last prefill row: max {diff.max():.3e} mean {diff.mean():.3e} "
+          f"identical elements {np.mean(gd == gl):.3f}", flush=True)
+    assert (diff <= bound).all(), f"max excess {(diff - bound).max():.3e}"
+    assert diff.mean() <= 3e-4, diff.mean()

@@ -3,8 +3,9 @@
 Bar: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3 over the
 compared rows, bf16 inputs and bf16 output.  The small cases span several
 tiles, partitions and ragged tails; the six workloads run at full size
-(every row for the decode and mixed steps; sampled rows, computed one by one
-by the oracle, for the 32K-token prompt and the shared-prefix step)."""
+(every row for the decode, mixed and shared-prefix steps; for the 32K-token
+prompt every row of its first two chunks and the first and last row of every
+32-position tile of the others; appended pools bit for bit)."""
 import math
 
 import numpy as np
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import compare, oracle_run, run_steps
+from gpu_util import compare, host_bits, oracle_run, run_steps
 
 pytestmark = pytest.mark.gpu
 
@@ -118,30 +119,75 @@ def test_full_workload(kvc, orc, cfg):
     print(f"{cfg}: max {mx:.3e} mean {mean:.3e}", flush=True)
 
 
-def _sample_rows(n, rng, k=6):
-    rows = {0, 1, n // 2, n - 2, n - 1} | set(rng.integers(0, n, size=k).tolist())
+def _tile_edge_rows(n, tile=32):
+    """First and last row of every `tile`-position block of an n-row chunk:
+    each prefill wave (and so each workgroup) of the chunk writes at least
+    two compared rows."""
     sel = np.zeros(n, dtype=bool)
-    sel[[r for r in rows if 0 <= r < n]] = True
+    sel[0::tile] = True
+    sel[tile - 1::tile] = True
+    sel[n - 1] = True
     return sel
 
 
-def test_long_prefill_chunks_sampled(kvc, orc):
-    """32768-token prompt in 16 chunks of 2048 (cached length 2048*k)."""
+@pytest.mark.timeout(900)
+def test_long_prefill_chunks(kvc, orc):
+    """32768-token prompt in 16 chunks of 2048 (cached length 2048*k): every
+    row of chunks 0 and 1, the first and last row of every 32-position tile
+    of chunks 2-15 (128 rows each), and the K/V pools after the 16 chunks bit
+    for bit against the oracle's appends."""
     wl = W.long_prefill()
-    g, _, _ = run_steps(kvc, wl)
-    rng = np.random.default_rng(5)
-    sels = [_sample_rows(st.total_q, rng) for st in wl.steps]
-    r, _, _ = oracle_run(orc, wl, row_select=sels)
+    g, kc, vc = run_steps(kvc, wl)
+    sels = [np.ones(st.total_q, dtype=bool) if k < 2 else _tile_edge_rows(st.total_q)
+            for k, st in enumerate(wl.steps)]
+    r, kp, vp = oracle_run(orc, wl, row_select=sels)
+    total = 0
     for k, (gk, rk, sel) in enumerate(zip(g, r, sels)):
-        compare(gk, rk, rows=sel, what=f"chunk {k}")
+        mx, mean = compare(gk, rk, rows=sel, what=f"chunk {k}")
+        total += int(sel.sum())
+        print(f"chunk {k}: {int(sel.sum())} of {sel.size} rows compared, max {mx:.3e} "
+              f"mean {mean:.3e}", flush=True)
+    assert np.array_equal(host_bits(kc), kp), "K pool after 16 chunks differs from the oracle's"
+    assert np.array_equal(host_bits(vc), vp), "V pool after 16 chunks differs from the oracle's"
+    print(f"long prompt: {total} rows compared; pools bit-exact ({kp.nbytes * 2} bytes)",
+          flush=True)
 
 
-def test_shared_prefix_sampled(kvc, orc):
-    """16 sequences over one refcounted 2048-token prefix, 256-token suffixes."""
-    wl = W.shared_prefix()
-    g, _, _ = run_steps(kvc, wl)
-    rng = np.random.default_rng(6)
-    sels = [_sample_rows(st.total_q, rng, k=40) for st in wl.steps]
-    r, _, _ = oracle_run(orc, wl, row_select=sels)
-    for k, (gk, rk, sel) in enumerate(zip(g, r, sels)):
-        compare(gk, rk, rows=sel, what=f"call {k}")
+@pytest.mark.timeout(900)
+def test_shared_prefix_all_rows_product_allocator(kvc, orc):
+    """16 sequences over one refcounted 2048-token prefix, 256-token suffixes.
+    The table comes from the product allocator: sequence 0 takes the prefix
+    blocks just in time, the other 15 share them by reference, and every
+    sequence then grows by its suffix blocks (kvc_extend_tables).  Checked
+    before any GPU work: 384 blocks in use instead of 2304, refcount 16 on
+    every prefix block, 1 on every suffix block.  Then every row of both
+    calls against the oracle, pools bit-exact, and every block freed."""
+    S, prefix, suffix, bs = 16, 2048, 256, 16
+    n_prefix, n_suffix = prefix // bs, suffix // bs
+    nb = n_prefix + S * n_suffix + 8
+    alloc = kvc.Allocator(nb, bs)
+    table = np.full((S, n_prefix + n_suffix), -1, dtype=np.int32)
+    held = np.zeros(S, dtype=np.int32)
+    held[0] = kvc.kvc_extend_table(alloc, table[0], 0, prefix)       # written once
+    for s in range(1, S):                                              # shared by reference
+        kvc.kvc_share_blocks(alloc, table[0, :n_prefix])
+        table[s, :n_prefix] = table[0, :n_prefix]
+        held[s] = n_prefix
+    kvc.kvc_extend_tables(alloc, table, held, np.full(S, prefix + suffix, dtype=np.int64))
+    used = nb - kvc.kvc_num_free_blocks(alloc)
+    assert used == 384 and S * (n_prefix + n_suffix) == 2304, used
+    assert all(kvc.kvc_block_refcount(alloc, int(b)) == S for b in table[0, :n_prefix])
+    assert all(kvc.kvc_block_refcount(alloc, int(b)) == 1 for b in table[:, n_prefix:].ravel())
+    assert len(np.unique(table[:, n_prefix:])) == S * n_suffix
+    wl = W.shared_prefix(table=table, num_blocks=nb)
+    g, kc, vc = run_steps(kvc, wl)
+    r, kp, vp = oracle_run(orc, wl)
+    for k, (gk, rk) in enumerate(zip(g, r)):
+        mx, mean = compare(gk, rk, what=f"call {k}")
+        print(f"shared prefix call {k}: all {gk.shape[0]} rows compared, max {mx:.3e} "
+              f"mean {mean:.3e}", flush=True)
+    assert np.array_equal(host_bits(kc), kp) and np.array_equal(host_bits(vc), vp)
+    for s in range(S):
+        kvc.kvc_free_blocks(alloc, table[s, :held[s]])
+    assert kvc.kvc_num_free_blocks(alloc) == nb
+    alloc.close()

@@ -303,21 +303,35 @@ def long_prefill(seed: int = 4, prompt: int = 32768, chunk: int = 2048) -> Workl
 
 
 def shared_prefix(seed: int = 4, num_seqs: int = 16, prefix: int = 2048,
-                  suffix: int = 256) -> Workload:
+                  suffix: int = 256, table: np.ndarray | None = None,
+                  num_blocks: int | None = None) -> Workload:
     """16 sequences share a 2048-token prefix (128 blocks, written once by the
     first call, a prefill of sequence 0 alone); the second call runs the 16
-    suffix chunks of 256 rows at cached length 2048 over the shared blocks."""
+    suffix chunks of 256 rows at cached length 2048 over the shared blocks.
+
+    ``table`` / ``num_blocks``: a block table [num_seqs, prefix/16 + suffix
+    blocks] built elsewhere (for instance by a block allocator, the prefix
+    blocks shared by every row) over a pool of num_blocks blocks, used
+    instead of the seeded permutation."""
     rng = np.random.default_rng(seed + 1000)
     hq, hkv, a, bs = 32, 8, 128, 16
     n_prefix = prefix // bs
     n_suffix = (suffix + bs - 1) // bs
-    nb = n_prefix + num_seqs * n_suffix + 8
-    perm = rng.permutation(nb).astype(np.int32)
     mb = n_prefix + n_suffix
-    table = np.empty((num_seqs, mb), dtype=np.int32)
-    table[:, :n_prefix] = perm[:n_prefix]
-    for s in range(num_seqs):
-        table[s, n_prefix:] = perm[n_prefix + s * n_suffix: n_prefix + (s + 1) * n_suffix]
+    if table is None:
+        nb = n_prefix + num_seqs * n_suffix + 8
+        perm = rng.permutation(nb).astype(np.int32)
+        table = np.empty((num_seqs, mb), dtype=np.int32)
+        table[:, :n_prefix] = perm[:n_prefix]
+        for s in range(num_seqs):
+            table[s, n_prefix:] = perm[n_prefix + s * n_suffix: n_prefix + (s + 1) * n_suffix]
+    else:
+        table = np.ascontiguousarray(table, dtype=np.int32)
+        nb = int(num_blocks)
+        if table.shape != (num_seqs, mb) or table.min() < 0 or table.max() >= nb:
+            raise ValueError("table must be [num_seqs, prefix + suffix blocks] of ids < num_blocks")
+        if not (table[:, :n_prefix] == table[:1, :n_prefix]).all():
+            raise ValueError("every row must start with the same prefix blocks")
     tq = prefix + num_seqs * suffix
     q = _normal_bf16(tq * hq * a, seed + 1000, "q").reshape(tq, hq, a)
     k_new = _normal_bf16(tq * hkv * a, seed + 1000, "k_new").reshape(tq, hkv, a)
@@ -337,6 +351,34 @@ def shared_prefix(seed: int = 4, num_seqs: int = 16, prefix: int = 2048,
                     block_size=bs, scale=1.0 / math.sqrt(a), k_pool=k_pool, v_pool=v_pool,
                     steps=[first, second],
                     extra={"prefix_blocks": n_prefix, "suffix_blocks": n_suffix})
+
+
+def split_into_calls(wl: Workload, per_call) -> Workload:
+    """The one step of ``wl`` fed as successive calls: ``per_call[k][s]`` new
+    rows of sequence s in call k (0 allowed), taken in order from the step's
+    rows of s, with the cached length advanced by the rows of earlier calls.
+    The pool and the table are unchanged (the table already covers the final
+    lengths)."""
+    st = wl.steps[0]
+    ql = st.q_lens
+    per_call = np.asarray(per_call, dtype=np.int64)
+    if per_call.ndim != 2 or per_call.shape[1] != st.num_seqs or (per_call < 0).any() \
+            or not (per_call.sum(axis=0) == ql).all():
+        raise ValueError("per_call must be [calls, num_seqs] and sum to each sequence's rows")
+    done = np.zeros(st.num_seqs, dtype=np.int64)
+    steps = []
+    for k in range(per_call.shape[0]):
+        rows = np.concatenate([np.arange(st.cu_seqlens_q[s] + done[s],
+                                         st.cu_seqlens_q[s] + done[s] + per_call[k, s])
+                               for s in range(st.num_seqs)]).astype(np.int64)
+        cu = np.zeros(st.num_seqs + 1, dtype=np.int32)
+        np.cumsum(per_call[k], out=cu[1:])
+        steps.append(Step(q=st.q[rows].copy(), k_new=st.k_new[rows].copy(),
+                          v_new=st.v_new[rows].copy(), cu_seqlens_q=cu,
+                          context_lens=(st.context_lens + done).astype(np.int32),
+                          block_table=st.block_table.copy()))
+        done += per_call[k]
+    return dataclasses.replace(wl, steps=steps)
 
 
 CONFIGS = {1: toy, 2: decode_mha, 3: decode_gqa, 4: mixed, 5: long_prefill, "5b": shared_prefix}

@@ -73,6 +73,9 @@ _sig("kvc_workspace_size", _SZ, [_I32] * 8)
 _sig("kvc_paged_attention_varlen", ctypes.c_int,
      [_P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
       _I32, _I32, ctypes.c_float, _P, _SZ, _P])
+_sig("kvc_paged_attention_varlen_noalloc", ctypes.c_int,
+     [_P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+      _I32, _I32, ctypes.c_float, _P])
 _sig("kvc_workspace_flags", ctypes.c_int, [_P, _P, ctypes.POINTER(_I32)])
 _sig("kvc_profile_begin", ctypes.c_int, [_I32])
 _sig("kvc_profile_end", ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)])
@@ -83,6 +86,7 @@ KVC_ERR_OOM = -2
 KVC_ERR_UNSUPPORTED = -3
 KVC_ERR_WORKSPACE = -4
 KVC_ERR_HIP = -5
+NOALLOC_SCRATCH_BYTES = 128 << 20  # KVC_NOALLOC_SCRATCH_BYTES of include/kvc.h
 
 EXPORTED = [
     "kvc_status_string", "kvc_last_error", "kvc_allocator_create", "kvc_allocator_destroy",
@@ -92,7 +96,7 @@ EXPORTED = [
     "kvc_scheduler_create", "kvc_scheduler_destroy", "kvc_scheduler_add", "kvc_scheduler_step",
     "kvc_scheduler_complete", "kvc_scheduler_num_waiting", "kvc_scheduler_num_running",
     "kvc_append_kv", "kvc_gather_kv", "kvc_workspace_size", "kvc_paged_attention_varlen",
-    "kvc_workspace_flags", "kvc_profile_begin", "kvc_profile_end",
+    "kvc_paged_attention_varlen_noalloc", "kvc_workspace_flags", "kvc_profile_begin", "kvc_profile_end",
 ]
 
 PROF_PHASES = ["plan", "append", "prefill", "decode", "merge"]
@@ -454,6 +458,46 @@ def kvc_paged_attention_varlen(out, q, k_new, v_new, k_cache, v_cache, block_tab
         _ptr(block_table), block_table.shape[1], _ptr(cu_seqlens_q), _ptr(context_lens), s, tq,
         int(max_q_len), int(max_context_len), hq, hkv, a, bs, float(scale), _ptr(workspace),
         workspace.numel(), _stream(stream)), "kvc_paged_attention_varlen")
+
+
+def _step_args(out, q, k_new, v_new, k_cache, v_cache, block_table, cu_seqlens_q,
+               context_lens):
+    """Checks shared by the attention entry points; returns the sizes."""
+    nb, hkv, bs, a = _cache_dims(k_cache, v_cache)
+    _need(q, torch.bfloat16, 3, "q")
+    _need(out, torch.bfloat16, 3, "out")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    if k_new is not None:
+        _need(k_new, torch.bfloat16, 3, "k_new")
+        _need(v_new, torch.bfloat16, 3, "v_new")
+        if tuple(k_new.shape) != (q.shape[0], hkv, a) or k_new.shape != v_new.shape:
+            raise ValueError("k_new/v_new must be [total_q, Hkv, A]")
+    _need(block_table, torch.int32, 2, "block_table")
+    _need(cu_seqlens_q, torch.int32, 1, "cu_seqlens_q")
+    _need(context_lens, torch.int32, 1, "context_lens")
+    tq, hq, a2 = q.shape
+    if a2 != a or out.shape != q.shape:
+        raise ValueError("q/out must be [total_q, Hq, A] with the cache's head_dim")
+    s = context_lens.shape[0]
+    if cu_seqlens_q.shape[0] != s + 1 or block_table.shape[0] != s:
+        raise ValueError("cu_seqlens_q must be [S+1] and block_table [S, max_blocks]")
+    return nb, hkv, bs, a, tq, hq, s
+
+
+def kvc_paged_attention_varlen_noalloc(out, q, k_new, v_new, k_cache, v_cache, block_table,
+                                       cu_seqlens_q, context_lens, scale, *, max_q_len,
+                                       max_context_len, stream=None):
+    """The step without a workspace: scratch is the library's static device
+    array (NOALLOC_SCRATCH_BYTES per GPU, shared by every call on that GPU, so
+    overlapping calls race); every kernel runs on ``stream``."""
+    nb, hkv, bs, a, tq, hq, s = _step_args(out, q, k_new, v_new, k_cache, v_cache, block_table,
+                                           cu_seqlens_q, context_lens)
+    _check(_lib.kvc_paged_attention_varlen_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), nb,
+        _ptr(block_table), block_table.shape[1], _ptr(cu_seqlens_q), _ptr(context_lens), s, tq,
+        int(max_q_len), int(max_context_len), hq, hkv, a, bs, float(scale), _stream(stream)),
+        "kvc_paged_attention_varlen_noalloc")
 
 
 def kvc_workspace_flags(workspace, stream=None) -> int:

@@ -301,6 +301,30 @@ int kvc_paged_attention_varlen(void* out, const void* q, const void* k_new, cons
                                float scale, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* No-allocation variant, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, meaning and result as
+ * kvc_paged_attention_varlen, without the workspace: the step's scratch is a
+ * static device array of KVC_NOALLOC_SCRATCH_BYTES that each GPU holds from
+ * the library's load until the process ends.  A step that needs more
+ * (kvc_workspace_size above the limit) returns KVC_ERR_WORKSPACE before
+ * anything is enqueued.  The call allocates nothing (no hipMalloc, no
+ * stream or event creation) and runs every kernel on `stream`, so its prefill
+ * does not overlap its decode.  Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (two streams, two threads)
+ * race, so callers serialise them.  The kernels' flags (see
+ * kvc_workspace_flags) go to the static array and are not reported. */
+#define KVC_NOALLOC_SCRATCH_BYTES (128u << 20)
+int kvc_paged_attention_varlen_noalloc(void* out, const void* q, const void* k_new,
+                                       const void* v_new, void* k_cache, void* v_cache,
+                                       int64_t num_blocks, const int32_t* block_table,
+                                       int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t total_q, int32_t max_q_len,
+                                       int32_t max_context_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, float scale, void* stream);
+
 /* Flags the kernels of the last call that used `workspace` raised (0 = none):
  *   1 a position beyond max_blocks_per_seq, 2 a block id outside
  *   [0, num_blocks), 4 more work than the host bounds allowed (lengths above

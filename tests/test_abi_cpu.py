@@ -118,3 +118,13 @@ def test_cache_bytes_matches_page_numbers(kvc):
     per_layer = kvc.kvc_cache_bytes(c13["tokens"] // 16, 16, c13["kv_heads"], c13["head_dim"], 2)
     assert round(per_layer * c13["layers"] / 1e9, 1) == c13["gb_rounded"]
     assert kvc.kvc_cache_bytes(-1, 16, 8, 128, 2) == -1
+
+
+def test_noalloc_scratch_limit_matches_the_header(kvc):
+    text = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    m = re.search(r"#define KVC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m, "KVC_NOALLOC_SCRATCH_BYTES not found in kvc.h"
+    assert kvc.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    # the headline mixed step (43 MB) fits; a 256-sequence MQA batch at 32K does not
+    assert kvc.kvc_workspace_size(516, 2560, 512, 4096, 32, 8, 128, 16) <= kvc.NOALLOC_SCRATCH_BYTES
+    assert kvc.kvc_workspace_size(256, 256, 1, 32768, 32, 1, 128, 16) > kvc.NOALLOC_SCRATCH_BYTES

@@ -77,6 +77,9 @@ _sig("kvc_paged_attention_varlen_noalloc", ctypes.c_int,
      [_P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
       _I32, _I32, ctypes.c_float, _P])
 _sig("kvc_workspace_flags", ctypes.c_int, [_P, _P, ctypes.POINTER(_I32)])
+_sig("kvc_padded_workspace_size", _SZ, [_I32] * 6)
+_sig("kvc_padded_decode_attention", ctypes.c_int,
+     [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _SZ, _P])
 _sig("kvc_profile_begin", ctypes.c_int, [_I32])
 _sig("kvc_profile_end", ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)])
 
@@ -96,7 +99,8 @@ EXPORTED = [
     "kvc_scheduler_create", "kvc_scheduler_destroy", "kvc_scheduler_add", "kvc_scheduler_step",
     "kvc_scheduler_complete", "kvc_scheduler_num_waiting", "kvc_scheduler_num_running",
     "kvc_append_kv", "kvc_gather_kv", "kvc_workspace_size", "kvc_paged_attention_varlen",
-    "kvc_paged_attention_varlen_noalloc", "kvc_workspace_flags", "kvc_profile_begin", "kvc_profile_end",
+    "kvc_paged_attention_varlen_noalloc", "kvc_workspace_flags",
+    "kvc_padded_workspace_size", "kvc_padded_decode_attention", "kvc_profile_begin", "kvc_profile_end",
 ]
 
 PROF_PHASES = ["plan", "append", "prefill", "decode", "merge"]
@@ -498,6 +502,42 @@ def kvc_paged_attention_varlen_noalloc(out, q, k_new, v_new, k_cache, v_cache, b
         _ptr(block_table), block_table.shape[1], _ptr(cu_seqlens_q), _ptr(context_lens), s, tq,
         int(max_q_len), int(max_context_len), hq, hkv, a, bs, float(scale), _stream(stream)),
         "kvc_paged_attention_varlen_noalloc")
+
+
+def kvc_padded_workspace_size(batch, n_max, num_q_heads, num_kv_heads, head_dim,
+                              block_size) -> int:
+    return int(_lib.kvc_padded_workspace_size(batch, n_max, num_q_heads, num_kv_heads, head_dim,
+                                              block_size))
+
+
+def kvc_padded_decode_attention(out, q, k_new, v_new, k_cache, v_cache, pad_lens, scale, *,
+                                n_max, workspace, stream=None):
+    """One decode step of a left-padded batch over a contiguous cache that
+    reserves n_max positions per sequence (k_cache/v_cache
+    [batch * n_max / block_size, Hkv, block_size, A], sequence b's pages
+    consecutive); pad_lens [batch] int32 on the GPU: sequence b's tokens sit
+    at positions pad_lens[b] .. n_max - 1."""
+    nb, hkv, bs, a = _cache_dims(k_cache, v_cache)
+    _need(q, torch.bfloat16, 3, "q")
+    _need(out, torch.bfloat16, 3, "out")
+    _need(pad_lens, torch.int32, 1, "pad_lens")
+    _need(workspace, torch.uint8, 1, "workspace")
+    b, hq, a2 = q.shape
+    if a2 != a or out.shape != q.shape or pad_lens.shape[0] != b:
+        raise ValueError("q/out must be [batch, Hq, A] with the cache's head_dim; pad_lens [batch]")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    if k_new is not None:
+        _need(k_new, torch.bfloat16, 3, "k_new")
+        _need(v_new, torch.bfloat16, 3, "v_new")
+        if tuple(k_new.shape) != (b, hkv, a) or k_new.shape != v_new.shape:
+            raise ValueError("k_new/v_new must be [batch, Hkv, A]")
+    if n_max % bs or nb != b * (n_max // bs):
+        raise ValueError("the cache must hold batch * n_max / block_size pages")
+    _check(_lib.kvc_padded_decode_attention(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(pad_lens), b, int(n_max), hq, hkv, a, bs, float(scale), _ptr(workspace),
+        workspace.numel(), _stream(stream)), "kvc_padded_decode_attention")
 
 
 def kvc_workspace_flags(workspace, stream=None) -> int:

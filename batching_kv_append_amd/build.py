@@ -25,8 +25,8 @@ PROBE_LIB = os.path.join(HERE, "libkvc_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["status.cpp", "allocator.cpp", "scheduler.cpp", "api.hip", "noalloc.hip", "cache_ops.hip",
-           "decode.hip", "prefill.hip"]
+SOURCES = ["status.cpp", "allocator.cpp", "scheduler.cpp", "api.hip", "noalloc.hip", "padded.hip",
+           "cache_ops.hip", "decode.hip", "prefill.hip"]
 PROBE_SOURCES = ["stream_probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",

@@ -408,9 +408,6 @@ extern "C" size_t kvc_workspace_size(int32_t num_seqs, int32_t total_q, int32_t 
 
 namespace kvc {
 
-// Checks and launches of one step (kvc_paged_attention_varlen and its
-// variants): `fn` names the entry point in error messages, `overlap` lets a
-// step with chunks and decode rows run its prefill on the side stream.
 int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
                     const void* v_new, void* k_cache, void* v_cache, int64_t num_blocks,
                     const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -418,7 +415,7 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
                     int32_t total_q, int32_t max_q_len, int32_t max_context_len,
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
-                    void* stream, bool overlap) {
+                    void* stream, bool overlap, const int32_t* key_start) {
     if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0)
         return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "negative size"));
     if (int rc = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, fn)) return rc;
@@ -426,6 +423,8 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
         return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "scale must be finite"));
     if ((k_new == nullptr) != (v_new == nullptr))
         return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "k_new and v_new must both be set or both NULL"));
+    if (key_start && (head_dim != 128 || max_q_len > 1))
+        return kvc_fail(KVC_ERR_UNSUPPORTED, fmt_msg(fn, "a key mask needs decode rows of head_dim 128"));
     if (num_seqs == 0 || total_q == 0) return KVC_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !context_lens)
         return kvc_fail(KVC_ERR_INVALID_ARG, fmt_msg(fn, "NULL pointer"));
@@ -479,6 +478,7 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
     a.head_dim = head_dim;
     a.block_size = block_size;
     a.scale = scale;
+    a.key_start = key_start;
     a.ws = (char*)workspace;
     a.lay = lay;
     a.stream = st;

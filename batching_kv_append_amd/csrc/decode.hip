@@ -290,6 +290,7 @@ struct DecodeParams {
     const int2* items;
     float* ws_ml;
     float* ws_acc;
+    const int32_t* key_start;  // left-padded batch: first key each sequence sees (else null)
     int64_t num_blocks;
     int32_t max_blocks, hq, hkv, G, HC;
     float scale_log2;  // scale * log2(e): scores live in the exp2 domain
@@ -531,7 +532,11 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // The two-group kernel is held to two waves per SIMD (at most 256 VGPRs; it
 // fits in 228 without spills): left free it takes about 300 and runs one wave
 // per SIMD, too few loads in flight for a memory-bound kernel.
-template <int BS, int NG>
+// MASKED (the left-padded batch): keys below key_start[s] are padding.  They
+// are still read (a padded batch streams every position), their scores are
+// excluded by select and their V rows are zeroed, so whatever the padding
+// holds has weight exactly 0.
+template <int BS, int NG, bool MASKED>
 __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(DecodeParams P) {
     constexpr int A = 128;
     constexpr int CPR = A / 8;              // 16-byte chunks per row
@@ -583,6 +588,8 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     const int nact = min(GP, (L - i0 + per_wave - 1) / per_wave);  // waves of this item with work
     const int nparts = ngroups == 1 ? nact : 2;  // 1: one wave holds the whole sequence
     const int t1 = min(L, t0 + per_wave);
+    // first unpadded key (at most L - 1: the new token is never padding)
+    const int kstart = MASKED ? min(max(P.key_start[s], 0), L - 1) : 0;
     const int h0 = kvh * P.G + hc * GW;
     const float cs = P.scale_log2;
     const bool pos_scale = cs > 0.f;
@@ -680,6 +687,14 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
                     vb[hh][j] = v_stream(vp + (min(tc + 4 * tg + j, t1 - 1) - t) * CPR);
             }
         }
+        const bool padded = MASKED && tc < kstart;  // some key of this step is padding
+        if (padded) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (tc + 4 * (g + 4 * hh) + j < kstart) vb[hh][j] = make_uint4(0, 0, 0, 0);
+        }
 
         // K rows into this wave's tile ([row][chunk ^ row % 16]), then the
         // A operands: lane (g, col) of block b, step ks takes chunk 4 ks + g
@@ -750,11 +765,11 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
 #pragma unroll
                 for (int r = 0; r < 8; ++r) v8[r] *= cs;
             }
-            if (tail) {
+            if (tail || padded) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const int t = tc + (r >> 2) * 16 + 4 * g + (r & 3);
-                    if (t >= t1) v8[r] = -INFINITY;
+                    if (t >= t1 || (MASKED && t < kstart)) v8[r] = -INFINITY;
                 }
             }
             float mx = fmaxf(fmaxf(fmaxf(v8[0], v8[1]), fmaxf(v8[2], v8[3])),
@@ -991,6 +1006,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
     }
 }
 
+template <int BS, bool MASKED>
+void launch_decode_mfma(const StepArgs& a, const DecodeParams& p, bool two, int grid) {
+    if (two) hipLaunchKernelGGL((decode_mfma_kernel<BS, 2, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<BS, 1, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
+}
+
 template <int A, int BS, int GW>
 void launch_decode_t(const StepArgs& a, const DecodeParams& p, int grid) {
     hipLaunchKernelGGL((decode_kernel<A, BS, GW>), dim3(grid), dim3(256), 0, a.stream, p);
@@ -1069,6 +1090,7 @@ hipError_t launch_decode(const StepArgs& a) {
     p.items = (const int2*)(ws + a.lay.dec_items);
     p.ws_ml = (float*)(ws + a.lay.ml);
     p.ws_acc = (float*)(ws + a.lay.acc);
+    p.key_start = a.key_start;
     p.num_blocks = a.num_blocks;
     p.max_blocks = a.max_blocks;
     p.hq = a.num_q_heads;
@@ -1087,12 +1109,12 @@ hipError_t launch_decode(const StepArgs& a) {
     if (a.head_dim == 128) {
         const bool two = GW > 16;  // 32 heads per wave: two MFMA column groups
         if (gp != 4) return hipErrorInvalidValue;  // the matrix decode works in partition groups
-        if (a.block_size == 16) {
-            if (two) hipLaunchKernelGGL((decode_mfma_kernel<16, 2>), dim3(grid), dim3(256), 0, a.stream, p);
-            else hipLaunchKernelGGL((decode_mfma_kernel<16, 1>), dim3(grid), dim3(256), 0, a.stream, p);
+        if (a.key_start) {
+            if (a.block_size == 16) launch_decode_mfma<16, true>(a, p, two, grid);
+            else launch_decode_mfma<4, true>(a, p, two, grid);
         } else {
-            if (two) hipLaunchKernelGGL((decode_mfma_kernel<4, 2>), dim3(grid), dim3(256), 0, a.stream, p);
-            else hipLaunchKernelGGL((decode_mfma_kernel<4, 1>), dim3(grid), dim3(256), 0, a.stream, p);
+            if (a.block_size == 16) launch_decode_mfma<16, false>(a, p, two, grid);
+            else launch_decode_mfma<4, false>(a, p, two, grid);
         }
     } else {
         if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);

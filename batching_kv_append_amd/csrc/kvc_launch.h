@@ -23,6 +23,7 @@ struct StepArgs {
     int32_t num_seqs, total_q, max_q_len, max_context_len;
     int32_t num_q_heads, num_kv_heads, head_dim, block_size;
     float scale;
+    const int32_t* key_start = nullptr;  // left-padded batch: first unpadded key per sequence
     char* ws;  // workspace base
     WsLayout lay;
     hipStream_t stream;
@@ -56,5 +57,21 @@ hipError_t launch_prefill(const StepArgs& a);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
+
+// Argument checks and launches of one step, shared by the entry points that
+// run it (kvc_paged_attention_varlen and its variants): `fn` names the entry
+// point in error messages; `overlap` lets a step with chunks and decode rows
+// run its prefill on the caller stream's side stream; `key_start` (device,
+// one per sequence, or null) masks each sequence's keys below it (a
+// left-padded batch; decode rows of head_dim 128 only).  Returns a
+// kvc_status.
+int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
+                    const void* v_new, void* k_cache, void* v_cache, int64_t num_blocks,
+                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t total_q, int32_t max_q_len, int32_t max_context_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
+                    void* stream, bool overlap, const int32_t* key_start = nullptr);
 
 }  // namespace kvc

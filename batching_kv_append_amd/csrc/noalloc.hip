@@ -29,19 +29,6 @@
 
 static __device__ __align__(256) unsigned char scratch[KVC_NOALLOC_SCRATCH_BYTES];
 
-namespace kvc {
-
-int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
-                    const void* v_new, void* k_cache, void* v_cache, int64_t num_blocks,
-                    const int32_t* block_table, int32_t max_blocks_per_seq,
-                    const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t num_seqs,
-                    int32_t total_q, int32_t max_q_len, int32_t max_context_len,
-                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
-                    void* stream, bool overlap);
-
-}  // namespace kvc
-
 namespace {
 
 constexpr int kMaxDevices = 64;

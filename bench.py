@@ -187,20 +187,29 @@ def run_serve(args, kvc):
 
 BASELINES_DESC = ("GQA decode batch (256 sequences, 32/8 heads, head_dim 128, context lognormal "
                   "median 1024, clip [16, 8192], block 16) run ragged and paged, against the "
-                  "same rows left-padded to the longest context, and the cache footprint of a "
-                  "contiguous max-length (8192) cache")
+                  "same rows as a left-padded batch (every sequence padded on the left to the "
+                  "longest, pad positions read and masked) and on a contiguous cache reserving "
+                  "8192 slots per sequence")
 
 
-def time_decode_batch(kvc, ctx, hq, hkv, a, bs, steps, warmup, seed=0, reserve_len=None):
+def time_decode_batch(kvc, ctx, hq, hkv, a, bs, steps, warmup, seed=0, reserve_len=None,
+                      padded=False):
     """Microseconds per call of one decode batch (one new token per sequence at
     the given contexts) on random GPU-drawn data.  Paged: each sequence holds
     just the blocks it needs, in shuffled pool order.  reserve_len set: a
     contiguous cache that reserves reserve_len slots per sequence (sequence i
-    owns the consecutive blocks i*R .. i*R+R-1, R = reserve_len / block)."""
+    owns the consecutive blocks i*R .. i*R+R-1, R = reserve_len / block).
+    padded: the left-padded batch (kvc_padded_decode_attention): every
+    sequence holds n_max = the longest one's length, rounded up to whole
+    blocks, its tokens right-aligned after pad positions that are read and
+    masked."""
     s = len(ctx)
     nblk = [-(-(int(c) + 1) // bs) for c in ctx]
     g = torch.Generator(device="cuda").manual_seed(seed)
-    if reserve_len is None:
+    if padded:
+        n_max = max(nblk) * bs
+        nb = s * max(nblk)
+    elif reserve_len is None:
         nb, mb = sum(nblk), max(nblk)
         perm = torch.randperm(nb, generator=g, device="cuda").to(torch.int32).cpu().numpy()
         table = np.full((s, mb), -1, np.int32)
@@ -218,15 +227,23 @@ def time_decode_batch(kvc, ctx, hq, hkv, a, bs, steps, warmup, seed=0, reserve_l
     q = torch.randn(s, hq, a, generator=g, device="cuda").to(torch.bfloat16)
     kn = torch.randn(s, hkv, a, generator=g, device="cuda").to(torch.bfloat16)
     vn = torch.randn(s, hkv, a, generator=g, device="cuda").to(torch.bfloat16)
-    cu = dev_i32(np.arange(s + 1))
-    cx = dev_i32(np.asarray(ctx))
-    tb = dev_i32(table)
-    mc = int(max(ctx))
-    ws = kvc.new_workspace(s, s, 1, mc, hq, hkv, a, bs)
     out = torch.empty_like(q)
-    call = lambda: kvc.kvc_paged_attention_varlen(  # noqa: E731
-        out, q, kn, vn, kc, vc, tb, cu, cx, 1.0 / math.sqrt(a), max_q_len=1, max_context_len=mc,
-        workspace=ws)
+    scale = 1.0 / math.sqrt(a)
+    if padded:
+        pad = dev_i32(np.array([n_max - (int(c) + 1) for c in ctx]))
+        ws = torch.empty(kvc.kvc_padded_workspace_size(s, n_max, hq, hkv, a, bs), dtype=torch.uint8,
+                         device="cuda")
+        call = lambda: kvc.kvc_padded_decode_attention(  # noqa: E731
+            out, q, kn, vn, kc, vc, pad, scale, n_max=n_max, workspace=ws)
+    else:
+        cu = dev_i32(np.arange(s + 1))
+        cx = dev_i32(np.asarray(ctx))
+        tb = dev_i32(table)
+        mc = int(max(ctx))
+        ws = kvc.new_workspace(s, s, 1, mc, hq, hkv, a, bs)
+        call = lambda: kvc.kvc_paged_attention_varlen(  # noqa: E731
+            out, q, kn, vn, kc, vc, tb, cu, cx, scale, max_q_len=1, max_context_len=mc,
+            workspace=ws)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -235,7 +252,8 @@ def time_decode_batch(kvc, ctx, hq, hkv, a, bs, steps, warmup, seed=0, reserve_l
         call()
     torch.cuda.synchronize()
     us = (time.perf_counter() - t0) * 1e6 / steps
-    assert kvc.kvc_workspace_flags(ws) == 0
+    if not padded:
+        assert kvc.kvc_workspace_flags(ws) == 0
     del kc, vc
     return us
 
@@ -251,8 +269,7 @@ def run_baselines(args, kvc):
     ctx = [int(c) for c in ctx]
     lens = [c + 1 for c in ctx]  # cached tokens after the step's append
     ragged_us = time_decode_batch(kvc, ctx, hq, hkv, a, bs, args.steps, args.warmup)
-    padded_us = time_decode_batch(kvc, [max(ctx)] * len(ctx), hq, hkv, a, bs, args.steps,
-                                  args.warmup)
+    padded_us = time_decode_batch(kvc, ctx, hq, hkv, a, bs, args.steps, args.warmup, padded=True)
     contiguous_us = time_decode_batch(kvc, ctx, hq, hkv, a, bs, args.steps, args.warmup,
                                       reserve_len=max_len + 1)
     useful, pads = base.left_padded_tokens(lens)
@@ -321,6 +338,60 @@ def algorithmic(wl, steps):
     return {"tokens": tokens, "decode_kv_bytes": dec_bytes, "prefill_pairs": pairs,
             "prefill_flops": 4 * a * hq * pairs,
             "append_bytes": tokens * hkv * a * 2 * 2 * 2}
+
+
+def chunks_only_step(st):
+    """The rows of the sequences of a step that bring >= 2 new tokens (its
+    prefill chunks), as a step of their own."""
+    ql = st.q_lens
+    keep = np.nonzero(ql >= 2)[0]
+    rows = np.concatenate([np.arange(st.cu_seqlens_q[s], st.cu_seqlens_q[s + 1]) for s in keep])
+    cu = np.zeros(len(keep) + 1, dtype=np.int32)
+    np.cumsum(ql[keep], out=cu[1:])
+    return W.Step(q=st.q[rows], k_new=st.k_new[rows], v_new=st.v_new[rows], cu_seqlens_q=cu,
+                  context_lens=st.context_lens[keep].copy(), block_table=st.block_table[keep].copy())
+
+
+def time_prefill_calls(kvc, wl, steps, stream, k_cache=None, v_cache=None, reps=2):
+    """The prefill kernel alone over chunks-only calls (no decode row, so the
+    prefill runs on the caller's stream with nothing beside it): its summed
+    duration per pass from HIP events around each launch, after one warm-up
+    pass.  Appending the chunks' rows again writes the same bytes."""
+    if k_cache is None:
+        k_cache, v_cache = dev_bits(wl.k_pool), dev_bits(wl.v_pool)
+    calls = []
+    for st in steps:
+        q = dev_bits(st.q)
+        calls.append(dict(out=torch.empty_like(q), q=q, k_new=dev_bits(st.k_new),
+                          v_new=dev_bits(st.v_new), table=dev_i32(st.block_table),
+                          cu=dev_i32(st.cu_seqlens_q), ctx=dev_i32(st.context_lens),
+                          ws=kvc.new_workspace(st.num_seqs, st.total_q, st.max_q_len,
+                                               st.max_context_len, wl.num_q_heads,
+                                               wl.num_kv_heads, wl.head_dim, wl.block_size),
+                          max_q=st.max_q_len, max_c=st.max_context_len))
+
+    def one_pass():
+        for c in calls:
+            kvc.kvc_paged_attention_varlen(c["out"], c["q"], c["k_new"], c["v_new"], k_cache,
+                                           v_cache, c["table"], c["cu"], c["ctx"], wl.scale,
+                                           max_q_len=c["max_q"], max_context_len=c["max_c"],
+                                           workspace=c["ws"], stream=stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+    kvc.kvc_profile_begin(reps * len(calls))
+    for _ in range(reps):
+        one_pass()
+    torch.cuda.synchronize()
+    phase_ms, n = kvc.kvc_profile_end()
+    assert n == reps * len(calls)
+    for c in calls:
+        assert kvc.kvc_workspace_flags(c["ws"]) == 0
+    flops = algorithmic(wl, steps)["prefill_flops"]
+    us = phase_ms["prefill"] * 1e3 / reps
+    tf = flops / (us * 1e-6) / 1e12
+    return {"calls": len(calls), "flops": flops, "kernel_us": us, "tflops": tf,
+            "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS}
 
 
 def cpu_model():
@@ -653,6 +724,19 @@ def main():
     cold_ms = [a.elapsed_time(b) for a, b in cold_ev]
     del scratch, sink
 
+    # Prefill alone: the step's chunks as a chunks-only call (the default
+    # mixed step's four 512-row chunks), and the 32768-token prompt's 16
+    # chunks, each with the prefill kernel timed by events around its launch.
+    prefill_standalone = None
+    if args.workload == "mixed":
+        sub = [chunks_only_step(st) for st in steps]
+        prefill_standalone = {
+            "mixed_step_chunks": time_prefill_calls(kvc, wl, sub, stream, k_cache, v_cache)}
+        lp = W.long_prefill()
+        prefill_standalone["long_prompt_16_chunks"] = time_prefill_calls(kvc, lp, lp.steps, stream)
+        del lp
+        torch.cuda.synchronize()
+
     alg = algorithmic(wl, steps)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = alg["tokens"] * args.steps / elapsed
@@ -698,6 +782,14 @@ def main():
                     "algorithmic_flops_per_launch": alg["prefill_flops"] / launches,
                     "avg_launch_us": pre_us / launches}
 
+    # The step's own floor: its decode bytes at the HBM peak plus its prefill
+    # flops at the matrix peak (the two overlap in the step, so this is a
+    # lower bound on its time), against the measured step.
+    floor_us = (alg["decode_kv_bytes"] / (HBM_PEAK_GBPS * 1e9)
+                + alg["prefill_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    step_roofline = {"decode_kv_bytes": alg["decode_kv_bytes"],
+                     "prefill_flops": alg["prefill_flops"], "floor_us": floor_us,
+                     "measured_us": ms_per_step * 1e3, "frac": floor_us / (ms_per_step * 1e3)}
     st0 = steps[0]
     result = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
@@ -713,6 +805,8 @@ def main():
                    "pool_blocks": wl.num_blocks},
         "roofline": roofline,
         "decode": decode, "prefill": prefill,
+        "prefill_standalone": prefill_standalone,
+        "step_roofline": step_roofline,
         # a phase with no work in this workload reports null: its empty launch
         # can sit behind the other stream's kernels, so its events time a wait
         "kernels_us_per_step": {

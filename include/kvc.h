@@ -333,6 +333,39 @@ int kvc_paged_attention_varlen_noalloc(void* out, const void* q, const void* k_n
 int kvc_workspace_flags(const void* workspace, void* stream, int32_t* flags);
 
 /* ------------------------------------------------------------------------
+ * The baseline that ragged continuous batching replaces: one decode step of
+ * a left-padded batch (news.myit.tw continuous-batching article, section
+ * "Continuous batching": the sequences of a static batch are padded on the
+ * left to one length and a padding mask hides the pad positions) over a
+ * contiguous cache that reserves n_max positions per sequence (klklkl10086
+ * kv_cache post, section "连续内存分配").  For comparison with the paged
+ * ragged step; it reads every position, pads included.
+ *   k_cache, v_cache: [batch * n_max / block_size][num_kv_heads][block_size]
+ *            [head_dim] bf16 (the pool's page format): sequence b owns pages
+ *            b * n_max / block_size .. (b + 1) * n_max / block_size - 1, its
+ *            position p in page p / block_size, slot p % block_size.
+ *   pad_lens: device int32 [batch]; sequence b's tokens sit at positions
+ *            pad_lens[b] .. n_max - 1 (values are clamped to [0, n_max - 1]).
+ *            Pad positions may hold anything: they get weight exactly 0.
+ *   q, out:  [batch][num_q_heads][head_dim]; k_new, v_new [batch][num_kv_heads]
+ *            [head_dim] are first appended at position n_max - 1 (NULL for
+ *            both: already in the cache).
+ * Row b of out is attention over keys pad_lens[b] .. n_max - 1 of sequence b,
+ * the same function kvc_paged_attention_varlen computes for a sequence of
+ * n_max - 1 - pad_lens[b] cached tokens.  head_dim 128, block_size 4 or 16,
+ * n_max a multiple of block_size (at most 2^24); otherwise
+ * KVC_ERR_UNSUPPORTED / KVC_ERR_INVALID_ARG, before anything is enqueued.
+ * workspace: kvc_padded_workspace_size(...) bytes, 256-byte aligned, caller
+ * owned (0 = arguments not supported). */
+size_t kvc_padded_workspace_size(int32_t batch, int32_t n_max, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size);
+int kvc_padded_decode_attention(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* pad_lens,
+                                int32_t batch, int32_t n_max, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Optional per-kernel timing (instrumentation; off by default).
  * kvc_profile_begin(n) makes the next n calls of kvc_paged_attention_varlen
  * record a HIP event just before and just after each of its kernels, on the

@@ -13,6 +13,8 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import workloads as W  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -67,3 +69,21 @@ def test_more_than_one_gpu_is_refused():
 def test_counter_summaries_match_their_workload_only(bench):
     for kernel in ("decode_mfma_kernel", "prefill_kernel"):
         assert bench.measured_traffic(kernel, "no_such_workload") is None
+
+
+def test_chunks_only_step_keeps_the_prefill_work(bench):
+    """The bench's stand-alone prefill timing runs the mixed step's chunks as
+    a call of their own: the same rows in the same order, all of the step's
+    prefill work and none of its decode work."""
+    wl = W.make_step_workload("m", [(0, 40), (300, 1), (17, 5), (1000, 1), (64, 130), (5, 0)],
+                              num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, seed=3)
+    st = wl.steps[0]
+    sub = bench.chunks_only_step(st)
+    assert sub.num_seqs == 3 and list(sub.q_lens) == [40, 5, 130]
+    assert list(sub.context_lens) == [0, 17, 64]
+    full = bench.algorithmic(wl, [st])
+    part = bench.algorithmic(wl, [sub])
+    assert part["prefill_flops"] == full["prefill_flops"] and part["decode_kv_bytes"] == 0
+    rows = np.r_[0:40, 41:46, 47:177]
+    assert np.array_equal(sub.q, st.q[rows]) and np.array_equal(sub.k_new, st.k_new[rows])
+    assert np.array_equal(sub.block_table, st.block_table[[0, 2, 4]])

@@ -66,8 +66,9 @@ int check_shape(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int
         std::snprintf(msg, sizeof msg, "%s: head ratio %d unsupported (1, 2 or a multiple of 4)", fn, G);
         return kvc_fail(KVC_ERR_UNSUPPORTED, msg);
     }
-    if (head_dim != 16 && head_dim != 128) {
-        std::snprintf(msg, sizeof msg, "%s: head_dim %d unsupported (16 or 128)", fn, head_dim);
+    if (head_dim != 16 && head_dim != 64 && head_dim != 128 && head_dim != 256) {
+        std::snprintf(msg, sizeof msg, "%s: head_dim %d unsupported (16, 64, 128 or 256)", fn,
+                      head_dim);
         return kvc_fail(KVC_ERR_UNSUPPORTED, msg);
     }
     if (block_size != 4 && block_size != 16) {

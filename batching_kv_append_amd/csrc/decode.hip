@@ -302,7 +302,7 @@ template <int A, int BS, int GW>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     constexpr int LPR = A / 8;      // lanes per token row (16 B per lane)
     constexpr int RPL = 64 / LPR;   // token rows per load instruction
-    constexpr int NL = (A == 128) ? 8 : 2;  // loads per chunk
+    constexpr int NL = (A == 128) ? 8 : (A == 256) ? 4 : 2;  // loads per chunk
     constexpr int CH = RPL * NL;    // tokens per chunk
     constexpr int NT = DECODE_PART / BS;  // table entries per partition (<= 64)
     constexpr bool UNIFORM_BLOCK = (BS % RPL) == 0;  // one block per load instruction
@@ -1117,8 +1117,21 @@ hipError_t launch_decode(const StepArgs& a) {
             else launch_decode_mfma<4, false>(a, p, two, grid);
         }
     } else {
-        if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);
-        else launch_decode_gw<16, 4>(a, p, GW, grid);
+        // the other head sizes take the vector-ALU decode (one partition per wave)
+        switch (a.head_dim) {
+            case 16:
+                if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);
+                else launch_decode_gw<16, 4>(a, p, GW, grid);
+                break;
+            case 64:
+                if (a.block_size == 16) launch_decode_gw<64, 16>(a, p, GW, grid);
+                else launch_decode_gw<64, 4>(a, p, GW, grid);
+                break;
+            default:
+                if (a.block_size == 16) launch_decode_gw<256, 16>(a, p, GW, grid);
+                else launch_decode_gw<256, 4>(a, p, GW, grid);
+                break;
+        }
     }
     return hipGetLastError();
 }
@@ -1134,10 +1147,12 @@ hipError_t launch_merge(const StepArgs& a) {
     mp.cap_dec = a.lay.cap_dec;
     mp.hq = a.num_q_heads;
     dim3 mgrid((unsigned)a.num_seqs, (unsigned)((a.num_q_heads + 3) / 4));
-    if (a.head_dim == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, a.stream, mp);
-    else
-        hipLaunchKernelGGL(merge_kernel<16>, mgrid, dim3(256), 0, a.stream, mp);
+    switch (a.head_dim) {
+        case 128: hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, a.stream, mp); break;
+        case 64: hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, a.stream, mp); break;
+        case 256: hipLaunchKernelGGL(merge_kernel<256>, mgrid, dim3(256), 0, a.stream, mp); break;
+        default: hipLaunchKernelGGL(merge_kernel<16>, mgrid, dim3(256), 0, a.stream, mp); break;
+    }
     return hipGetLastError();
 }
 

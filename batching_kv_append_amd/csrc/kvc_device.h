@@ -102,11 +102,13 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
 }
 
-// Sum over groups of LANES consecutive lanes (LANES in {2, 4, 8, 16}) with DPP
-// row operations; every lane of a group ends with the group's sum.
+// Sum over groups of LANES consecutive lanes (LANES in {2, 4, 8, 16, 32}) with
+// DPP row operations (and one lane exchange across rows for 32); every lane of
+// a group ends with the group's sum.
 template <int LANES>
 __device__ __forceinline__ float group_sum(float x) {
-    static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16, "group size");
+    static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32,
+                  "group size");
     // quad_perm [1,0,3,2]: swap neighbours
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
     if constexpr (LANES >= 4)  // quad_perm [2,3,0,1]: swap pairs
@@ -115,6 +117,8 @@ __device__ __forceinline__ float group_sum(float x) {
         x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
     if constexpr (LANES >= 16)  // row_mirror: lane i <-> 15-i, joins the two halves
         x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+    if constexpr (LANES >= 32)  // lane i <-> i ^ 16: joins two rows of 16
+        x += __shfl_xor(x, 16, 64);
     return x;
 }
 

@@ -126,18 +126,22 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)const_cast<char*>(p));
 }
 
+// head_dim 256 doubles the accumulators and the Q^T operand: one workgroup
+// (128 KiB of LDS) per compute unit.
 template <int A, int BS, int HPW>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
+__global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillParams P) {
     constexpr int TK = PREFILL_TK;         // keys per tile (64)
     constexpr int CPR = A / 8;             // 16-byte chunks per K/V row
     constexpr int KK = A / 16;             // 16-dim MFMA steps of QK^T
     constexpr int DT = (A + 31) / 32;      // 32-dim output tiles
     constexpr int QW = PREFILL_QW;         // positions per wave (32)
     constexpr int SPAN = QW * (4 / HPW);   // positions per workgroup
-    constexpr int LOADERS = (TK / 4) * CPR;  // threads that each load 4 keys x 8 dims
+    constexpr int KGC = (TK / 4) * CPR;    // (4-key group, 16-byte chunk) loads of a tile
+    constexpr int NKC = (KGC + 255) / 256; // of them per thread (2 for head_dim 256)
+    constexpr int LOADERS = KGC < 256 ? KGC : 256;  // threads that load
     constexpr float NEG_BIG = -1.0e30f;
     constexpr float RESCALE_SLACK = 8.0f;  // log2 units: weights stay < 2^8
-    static_assert(LOADERS <= 256, "tile loaders");
+    static_assert(KGC == LOADERS * NKC, "tile loaders");
     static_assert(BS % 4 == 0, "4 consecutive keys must share a block");
 
     __shared__ uint4 sK[2][TK * CPR];  // [key][chunk ^ (key % CPR)]
@@ -199,11 +203,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
     // never meets a non-finite value.
     const bool loader = tid < LOADERS;
     // Thread -> (key group kg: keys 4kg .. 4kg+3, 16-byte chunk cc: dims
-    // 8cc .. 8cc+7).  Wave w covers key groups 4w .. 4w+3.  For A = 128 each
-    // 16-lane group holds chunks 8h .. 8h+7 of key groups kg and kg ^ 2, so
-    // its 16-byte stores (one row per store) hit 16 distinct bank groups.
+    // 8cc .. 8cc+7; with head_dim 256 also chunk cc + 16).  Wave w covers key
+    // groups 4w .. 4w+3.  For A >= 128 each 16-lane group holds chunks
+    // 8h .. 8h+7 of key groups kg and kg ^ 2, so its 16-byte stores (one row
+    // per store) hit 16 distinct bank groups.
     int kg, cc;
-    if constexpr (CPR == 16) {
+    if constexpr (CPR >= 16) {
         kg = ((tid >> 5) & 1) | (((tid >> 3) & 1) << 1) | ((tid >> 6) << 2);
         cc = (tid & 7) | (((tid >> 4) & 1) << 3);
     } else {
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
     // offset (16-byte units) of the thread's first row inside a cache block
     const uint32_t toff = (uint32_t)((kvh * BS + (4 * kg) % BS) * CPR + cc);
     const uint32_t blk_stride = (uint32_t)(P.hkv * BS * CPR);
-    u32x4_t kreg[4], vreg[4];  // native vectors: the staging stays in VGPRs
+    u32x4_t kreg[4 * NKC], vreg[4 * NKC];  // native vectors: the staging stays in VGPRs
     int bad = 0;
     // Block-table entry of this thread's key group in the tile at k0 (-1 past
     // the table).  Read one tile ahead of its use, so the K/V addresses never
@@ -236,24 +241,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams P) {
         const uint4* kp = P.k_cache + base;
         const uint4* vp = P.v_cache + base;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            kreg[j] = __builtin_bit_cast(u32x4_t, kp[j * CPR]);
-            vreg[j] = __builtin_bit_cast(u32x4_t, vp[j * CPR]);
-        }
+        for (int c = 0; c < NKC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kreg[c * 4 + j] = __builtin_bit_cast(u32x4_t, kp[j * CPR + c * 16]);
+                vreg[c * 4 + j] = __builtin_bit_cast(u32x4_t, vp[j * CPR + c * 16]);
+            }
     };
     auto store_tile = [&](int buf, int k0) __attribute__((always_inline)) {
         if (!loader) return;
         if (k0 + 4 * kg + 3 >= L) {  // the sequence's last keys: V rows past L are zero
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (k0 + 4 * kg + j >= L) vreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+            for (int c = 0; c < NKC; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (k0 + 4 * kg + j >= L) vreg[c * 4 + j] = u32x4_t{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = 4 * kg + j;
-            sK[buf][key * CPR + (cc ^ (key % CPR))] = __builtin_bit_cast(uint4, kreg[j]);
-            sV[buf][key * CPR + (cc ^ vswz<CPR>(key))] = __builtin_bit_cast(uint4, vreg[j]);
-        }
+        for (int c = 0; c < NKC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int key = 4 * kg + j;
+                const int ch = cc + c * 16;
+                sK[buf][key * CPR + (ch ^ (key % CPR))] = __builtin_bit_cast(uint4, kreg[c * 4 + j]);
+                sV[buf][key * CPR + (ch ^ vswz<CPR>(key))] = __builtin_bit_cast(uint4, vreg[c * 4 + j]);
+            }
     };
     // Transposing-read offsets (bytes inside a V tile) of this lane for the
     // V^T operand of output tile dt, keys 8 rd + {0..3} of a 16-key step: the
@@ -480,12 +492,24 @@ hipError_t launch_prefill(const StepArgs& a) {
     if (gx <= 0) return hipSuccess;
     if (gx > INT32_MAX) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx);
-    if (a.head_dim == 128) {
-        if (a.block_size == 16) launch_prefill_hpw<128, 16>(a, p, hpw, grid);
-        else launch_prefill_hpw<128, 4>(a, p, hpw, grid);
-    } else {
-        if (a.block_size == 16) launch_prefill_hpw<16, 16>(a, p, hpw, grid);
-        else launch_prefill_hpw<16, 4>(a, p, hpw, grid);
+    const bool b16 = a.block_size == 16;
+    switch (a.head_dim) {
+        case 128:
+            if (b16) launch_prefill_hpw<128, 16>(a, p, hpw, grid);
+            else launch_prefill_hpw<128, 4>(a, p, hpw, grid);
+            break;
+        case 64:
+            if (b16) launch_prefill_hpw<64, 16>(a, p, hpw, grid);
+            else launch_prefill_hpw<64, 4>(a, p, hpw, grid);
+            break;
+        case 256:
+            if (b16) launch_prefill_hpw<256, 16>(a, p, hpw, grid);
+            else launch_prefill_hpw<256, 4>(a, p, hpw, grid);
+            break;
+        default:
+            if (b16) launch_prefill_hpw<16, 16>(a, p, hpw, grid);
+            else launch_prefill_hpw<16, 4>(a, p, hpw, grid);
+            break;
     }
     return hipGetLastError();
 }

@@ -70,7 +70,7 @@
  *             variable KVC_DEBUG=1 the host also copies the lengths and the
  *             table back (synchronously) and rejects bad values with
  *             KVC_ERR_INVALID_ARG before launching.
- *   Supported head_dim in {16, 128}; block_size in {4, 16};
+ *   Supported head_dim in {16, 64, 128, 256}; block_size in {4, 16};
  *             num_q_heads % num_kv_heads == 0 with ratio G = 1, 2 or any
  *             multiple of 4 (MHA, GQA, MQA).  Others return
  *             KVC_ERR_UNSUPPORTED.

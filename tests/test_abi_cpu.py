@@ -55,7 +55,9 @@ def test_workspace_size_grows_with_the_step(kvc):
     assert base > 0
     assert kvc.kvc_workspace_size(128, 128, 1, 4096, 32, 32, 128, 16) > base
     assert kvc.kvc_workspace_size(64, 64, 1, 8192, 32, 32, 128, 16) > base
-    assert kvc.kvc_workspace_size(64, 64, 1, 4096, 32, 32, 64, 16) == 0   # head_dim 64
+    assert kvc.kvc_workspace_size(64, 64, 1, 4096, 32, 32, 64, 16) > 0    # head_dim 64
+    assert kvc.kvc_workspace_size(64, 64, 1, 4096, 32, 32, 256, 16) > 0   # head_dim 256
+    assert kvc.kvc_workspace_size(64, 64, 1, 4096, 32, 32, 96, 16) == 0   # head_dim 96
     assert kvc.kvc_workspace_size(64, 64, 1, 4096, 32, 32, 128, 8) == 0   # block size 8
     assert kvc.kvc_workspace_size(64, 64, 1, 4096, 30, 10, 128, 16) == 0  # ratio 3
     assert kvc.kvc_workspace_size(-1, 64, 1, 4096, 32, 32, 128, 16) == 0
@@ -72,7 +74,7 @@ def _raw_varlen(kvc, **over):
 
 def test_varlen_rejects_before_launch(kvc):
     # unsupported shapes are reported even with NULL pointers
-    assert _raw_varlen(kvc, a=64) == kvc.KVC_ERR_UNSUPPORTED
+    assert _raw_varlen(kvc, a=96) == kvc.KVC_ERR_UNSUPPORTED
     assert _raw_varlen(kvc, bs=32) == kvc.KVC_ERR_UNSUPPORTED
     assert _raw_varlen(kvc, hq=6, hkv=4) == kvc.KVC_ERR_INVALID_ARG
     assert _raw_varlen(kvc, hq=12, hkv=4) == kvc.KVC_ERR_UNSUPPORTED
@@ -96,7 +98,7 @@ def test_varlen_rejects_before_launch(kvc):
 
 def test_append_and_gather_reject_before_launch(kvc):
     lib = kvc._lib
-    assert lib.kvc_append_kv(None, None, None, None, 1, None, 1, None, None, 1, 1, 4, 64, 16,
+    assert lib.kvc_append_kv(None, None, None, None, 1, None, 1, None, None, 1, 1, 4, 96, 16,
                              None) == kvc.KVC_ERR_UNSUPPORTED
     assert lib.kvc_append_kv(None, None, None, None, 1, None, 1, None, None, 1, 1, 4, 128, 16,
                              None) == kvc.KVC_ERR_INVALID_ARG

@@ -21,6 +21,8 @@ SMALL = [
     ("ragged_a16_bs4", [(5, 3), (0, 4), (9, 1), (16, 2), (0, 0), (31, 17)], 3, 16, 4),
     ("ragged_a128_bs4", [(1, 70), (64, 1), (3, 3)], 8, 128, 4),
     ("ragged_a16_bs16", [(0, 33), (15, 2), (16, 1)], 1, 16, 16),
+    ("ragged_a64_bs4", [(5, 3), (0, 4), (9, 1), (16, 2), (0, 0), (31, 17)], 2, 64, 4),
+    ("ragged_a256_bs16", [(0, 33), (15, 2), (16, 1), (40, 0), (3, 20)], 3, 256, 16),
 ]
 
 

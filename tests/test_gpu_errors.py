@@ -81,11 +81,11 @@ def test_bad_arguments_enqueue_nothing(kvc):
                                        wl.scale, max_q_len=st.total_q + 1,
                                        max_context_len=st.max_context_len, workspace=ws)
     assert e.value.status == kvc.KVC_ERR_INVALID_ARG
-    # head_dim 64 is not built
-    k64 = torch.zeros(wl.num_blocks, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
-    q64 = torch.zeros(st.total_q, 8, 64, dtype=torch.bfloat16, device="cuda")
+    # head_dim 96 is not built
+    k96 = torch.zeros(wl.num_blocks, 2, 16, 96, dtype=torch.bfloat16, device="cuda")
+    q96 = torch.zeros(st.total_q, 8, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(kvc.KvcError) as e:
-        kvc.kvc_paged_attention_varlen(torch.zeros_like(q64), q64, None, None, k64, k64.clone(),
+        kvc.kvc_paged_attention_varlen(torch.zeros_like(q96), q96, None, None, k96, k96.clone(),
                                        d.table, d.cu, d.ctx, wl.scale, **kw)
     assert e.value.status == kvc.KVC_ERR_UNSUPPORTED
     torch.cuda.synchronize()

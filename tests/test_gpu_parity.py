@@ -63,6 +63,19 @@ SMALL = [
     ("bound_chunks_only", [(50, 4), (300, 2)], 8, 2, 128, 16),
     ("bound_empty_seq", [(50, 4), (300, 0), (10, 3), (2000, 1)], 8, 2, 128, 16),
     ("a16_bound_one_decode", [(9, 3), (40, 1)], 2, 1, 16, 4),
+    # head dims 64 and 256, block sizes 4 and 16, G = 1, 4 and 32
+    ("a64_decode_g1_bs16", [(c, 1) for c in DEC_LENS], 4, 4, 64, 16),
+    ("a64_decode_g4_bs4", [(c, 1) for c in DEC_LENS], 8, 2, 64, 4),
+    ("a64_decode_g32", [(c, 1) for c in DEC_LENS[:9]], 32, 1, 64, 16),
+    ("a64_prefill_g1_bs4", PRE_SPECS, 2, 2, 64, 4),
+    ("a64_prefill_g4_bs16", PRE_SPECS, 8, 2, 64, 16),
+    ("a64_mixed_g32_bs16", MIXED_SPECS, 32, 1, 64, 16),
+    ("a256_decode_g1_bs16", [(c, 1) for c in DEC_LENS], 2, 2, 256, 16),
+    ("a256_decode_g4_bs4", [(c, 1) for c in DEC_LENS], 8, 2, 256, 4),
+    ("a256_decode_g32", [(c, 1) for c in DEC_LENS[:9]], 32, 1, 256, 16),
+    ("a256_prefill_g1_bs16", PRE_SPECS, 2, 2, 256, 16),
+    ("a256_prefill_g4_bs4", PRE_SPECS, 8, 2, 256, 4),
+    ("a256_mixed_g32_bs4", MIXED_SPECS, 32, 1, 256, 4),
 ]
 
 

@@ -1,6 +1,7 @@
 """Seeded random shapes against the oracle: many small ragged batches that mix
 decode rows, prompt chunks and empty rows, over the supported head groupings
-(G = 1, 2 or a multiple of 4), block sizes 4 and 16 and head dims 16 and 128,
+(G = 1, 2 or a multiple of 4), block sizes 4 and 16 and head dims 16, 64, 128
+and 256,
 with context lengths drawn around block, tile and partition boundaries.  Same
 bar as the other parity tests (max |diff| <= 2e-2, mean <= 2e-3); the pools
 after the call equal the oracle's bit for bit."""
@@ -18,11 +19,11 @@ N_CASES = 24
 EDGES = [0, 1, 3, 4, 5, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513]
 
 
-def _case(i):
+def _case(i, dims=None):
     rng = np.random.default_rng(1000 + i)
     g = int(rng.choice([1, 2, 4, 8, 12, 16, 32, 64]))
     hkv = int(rng.choice([1, 2, 3])) if g <= 16 else 1
-    a = 16 if rng.random() < 0.25 else 128
+    a = (16 if rng.random() < 0.25 else 128) if dims is None else int(rng.choice(dims))
     bs = int(rng.choice([4, 16]))
     n = int(rng.integers(1, 13))
     specs = []
@@ -43,6 +44,8 @@ def _case(i):
 
 
 CASES = [_case(i) for i in range(N_CASES)]
+# head dims 64 and 256 (the vector-ALU decode and the prefill instances of those sizes)
+CASES += [_case(i, dims=(64, 256)) for i in range(N_CASES, N_CASES + 12)]
 
 
 @pytest.fixture(scope="module")

@@ -6,9 +6,10 @@
 // decode stage is limited by memory access; clvsit.github.io AWS SageMaker
 // page: every step moves the parameters and the cache into the compute
 // units).  The kernels therefore aim at HBM bandwidth:
-//   * a sequence's context is cut into pieces of at most DECODE_PART tokens
-//     (split-K), a cut that depends only on its own length, so even a short
-//     batch of long contexts yields thousands of independent pieces of work;
+//   * a sequence's context is cut into pieces of at most decode_part(head_dim)
+//     tokens (split-K), a cut that depends only on its own length, so even a
+//     short batch of long contexts yields thousands of independent pieces of
+//     work;
 //     the partial softmax states are combined by an exact log-sum-exp merge
 //     (an exact regrouping of the row-wise softmax of the "Attention" section
 //     of the continuous-batching article);
@@ -17,13 +18,13 @@
 //   * the GW query heads that share a kv head (GQA, e2hang/Notes "MQA与GQA")
 //     are served from one read of K/V;
 //   * head_dim 128 (decode_mfma_kernel): a sequence is cut into
-//     ceil(L / 1024) work items of equal length, and a workgroup takes one
+//     ceil(L / 4096) work items of equal length, and a workgroup takes one
 //     item of one (sequence, kv head, head chunk), a quarter of it per wave
-//     (at most one partition), scores and P.V on bf16 MFMA; the four states
-//     are combined in LDS, so split-K partials (and the merge) exist per
-//     item;
-//   * head_dim 16 (decode_kernel): one wave per partition, 16 lanes per
-//     token row, dot products reduced with DPP row operations.
+//     (at most one 1024-token partition), scores and P.V on bf16 MFMA; the
+//     four states are combined in LDS, so split-K partials (and the merge)
+//     exist per item;
+//   * head_dim 16, 64 and 256 (decode_kernel): one wave per 256-token
+//     partition, dot products reduced across the lanes of a token row.
 // The planning kernel lists the work items on the device, longest pieces
 // first, so the host needs no copy of the lengths, and the hardware
 // dispatcher hands the next workgroup to whichever compute unit frees up
@@ -42,14 +43,15 @@ namespace {
 constexpr int PLAN_THREADS = 1024;
 
 constexpr int COST_BUCKETS = 1024;  // prefill cost histogram (key tiles, clamped)
-constexpr int DEC_BUCKETS = DECODE_PART / 32;  // decode order: 32-token steps per wave
+constexpr int DEC_BUCKETS = DECODE_PART_MFMA / 32;  // decode order: 32-token steps per wave
 
 struct PrepParams {
     // planning
     const int32_t* cu;
     const int32_t* ctx;
     int32_t num_seqs, total_q, max_q_len, max_context_len, span;
-    int32_t gp;  // decode partitions per work item
+    int32_t gp;     // decode partitions per work item
+    int32_t dpart;  // decode partition length (tokens)
     int64_t cap_dec, cap_pre;
     int32_t* hdr;
     int2* dec_items;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     const int32_t* __restrict__ cu = P.cu;
     const int32_t* __restrict__ ctx = P.ctx;
     const int32_t num_seqs = P.num_seqs, total_q = P.total_q, max_q_len = P.max_q_len;
-    const int32_t max_context_len = P.max_context_len, span = P.span, gp = P.gp;
+    const int32_t max_context_len = P.max_context_len, span = P.span, gp = P.gp, dpart = P.dpart;
     const int64_t cap_dec = P.cap_dec, cap_pre = P.cap_pre;
     int32_t* hdr = P.hdr;
     int2* dec_items = P.dec_items;
@@ -143,9 +145,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
         const int L = c + 1;
         if (gp == 1) {
             bucket = 0;
-            return (L + DECODE_PART - 1) / DECODE_PART;
+            return (L + dpart - 1) / dpart;
         }
-        const int ng = (L + gp * DECODE_PART - 1) / (gp * DECODE_PART);
+        const int ng = (L + gp * dpart - 1) / (gp * dpart);
         const int per_wave = ((L + gp * ng - 1) / (gp * ng) + 31) / 32;  // in 32-token steps
         bucket = min(per_wave, DEC_BUCKETS) - 1;
         return ng;
@@ -304,9 +306,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     constexpr int RPL = 64 / LPR;   // token rows per load instruction
     constexpr int NL = (A == 128) ? 8 : (A == 256) ? 4 : 2;  // loads per chunk
     constexpr int CH = RPL * NL;    // tokens per chunk
-    constexpr int NT = DECODE_PART / BS;  // table entries per partition (<= 64)
+    constexpr int DP = DECODE_PART_VALU;  // partition length
+    constexpr int NT = DP / BS;           // table entries per partition (<= 64)
     constexpr bool UNIFORM_BLOCK = (BS % RPL) == 0;  // one block per load instruction
-    static_assert(DECODE_PART % CH == 0, "chunk must divide the partition");
+    static_assert(DP % CH == 0, "chunk must divide the partition");
     static_assert(NT <= 64, "table slice must fit one VGPR");
 
     const int lane = threadIdx.x & 63;
@@ -326,9 +329,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
         const int s = it.x, part = it.y;
         const int L = P.ctx[s] + 1;
         const int row = P.cu[s];
-        const int nparts = (L + DECODE_PART - 1) / DECODE_PART;
-        const int t0 = part * DECODE_PART;
-        const int t1 = min(L, t0 + DECODE_PART);
+        const int nparts = (L + DP - 1) / DP;
+        const int t0 = part * DP;
+        const int t1 = min(L, t0 + DP);
         const int h0 = kvh * P.G + hc * GW;
 
         // table slice of this partition: lane i holds entry (t0 / BS + i)
@@ -523,7 +526,7 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // head, as in MQA): the groups share every K fragment and the V^T tile, so
 // the partition's K/V is read once for all of them.
 // A workgroup is one work item of one (sequence, kv head, head chunk).  The
-// sequence's ceil(L / (GP x DECODE_PART)) items split it evenly, and wave w
+// sequence's ceil(L / (GP x DP)) items split it evenly, and wave w
 // takes the w-th quarter of its item (a multiple of 32 tokens, at most one
 // partition), so a short sequence keeps all four waves busy for a short time
 // instead of one wave for a long one.  The last of the item's waves to finish
@@ -541,9 +544,10 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     constexpr int A = 128;
     constexpr int CPR = A / 8;              // 16-byte chunks per row
     constexpr int STEP = 32;                // tokens per matrix step
-    constexpr int NT = DECODE_PART / BS;    // table entries per partition
+    constexpr int DP = DECODE_PART_MFMA;    // partition length: at most one wave's tokens
+    constexpr int NT = DP / BS;             // table entries per wave, at most
+    constexpr int NTV = (NT + 63) / 64;     // VGPRs holding them (4 for 4-token blocks)
     constexpr float RESCALE_SLACK = 8.0f;   // log2 units: weights stay < 2^8
-    static_assert(NT <= 64, "table slice must fit one VGPR");
     static_assert(BS % 4 == 0, "4 consecutive tokens must share a block");
 
     constexpr int GP = DECODE_GROUP;        // waves per work item (at most a partition each)
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     // last one fewer) and each wave a quarter of that, a multiple of STEP
     // tokens and at most one partition.  Item count and split depend only on
     // the sequence's own length.
-    const int ngroups = (L + GP * DECODE_PART - 1) / (GP * DECODE_PART);  // work items of the sequence
+    const int ngroups = (L + GP * DP - 1) / (GP * DP);  // work items of the sequence
     const int per_wave = ((L + GP * ngroups - 1) / (GP * ngroups) + STEP - 1) / STEP * STEP;
     const int span = GP * per_wave;
     const int i0 = it.y * span;
@@ -594,14 +598,19 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     const float cs = P.scale_log2;
     const bool pos_scale = cs > 0.f;
 
-    // table slice: lane i holds entry (t0 / BS + i)
+    // table slice: lane i of register v holds entry (t0 / BS + 64 v + i)
     const int lb0 = t0 / BS;
     const int nlb = (t1 - t0 + BS - 1) / BS;
-    int tbl = -1, short_tbl = 0;  // short_tbl: a needed block is past the table row
-    if (lane < nlb && lane < NT) {
-        const int64_t lb = lb0 + lane;
-        if (lb < P.max_blocks) tbl = P.table[(int64_t)s * P.max_blocks + lb];
-        else short_tbl = 1;
+    int tbl[NTV], short_tbl = 0;  // short_tbl: a needed block is past the table row
+#pragma unroll
+    for (int v = 0; v < NTV; ++v) {
+        tbl[v] = -1;
+        const int i = 64 * v + lane;
+        if (i < nlb) {
+            const int64_t lb = lb0 + i;
+            if (lb < P.max_blocks) tbl[v] = P.table[(int64_t)s * P.max_blocks + lb];
+            else short_tbl = 1;
+        }
     }
 
     // Q^T operand of group ng: column col = head h0 + 16ng + col (zero past
@@ -630,16 +639,20 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     }
     int bad = 0;
 
-    // Block id of token t (< t1) through the table slice.  With 16-token
-    // blocks every lane of a 16-token group asks for the same block, so the
-    // caller passes the group's first (clamped) token and a uniform readlane
-    // serves it; smaller blocks take a per-lane shuffle.
-    auto block_of = [&](int t, int t_group) -> int64_t {
+    // Block id of token t (< t1) through the table slice register tv, the
+    // one that holds the current step's entries.  A step's entries never
+    // straddle two registers: it starts a multiple of 32 tokens past t0, so
+    // its first entry is a multiple of 32 / BS, which divides 64.  With
+    // 16-token blocks every lane of a 16-token group asks for the same block,
+    // so the caller passes the group's first (clamped) token and a uniform
+    // readlane serves it; smaller blocks take a per-lane shuffle.
+    auto block_of = [&](int tv, int t, int t_group) -> int64_t {
         if constexpr (BS == 16) {
-            return __builtin_amdgcn_readlane(tbl, t_group / BS - lb0);
+            static_assert(NTV == 1, "one register of entries");
+            return __builtin_amdgcn_readlane(tv, t_group / BS - lb0);
         } else {
             (void)t_group;
-            return __shfl(tbl, (t / BS - lb0) & 63, 64);
+            return __shfl(tv, (t / BS - lb0) & 63, 64);
         }
     };
 
@@ -655,6 +668,13 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             reinterpret_cast<const u32x4_t*>(ptr)));
     };
     for (int tc = t0; tc < t1; tc += STEP) {
+        int tv = tbl[0];  // the table register of this step (a uniform choice)
+        {
+            const int sel = ((tc - t0) / BS) >> 6;
+#pragma unroll
+            for (int v = 1; v < NTV; ++v)
+                if (sel == v) tv = tbl[v];
+        }
         // ---- K: 32 rows, four per load, each row whole (16 lanes x 16 B) --
         // Lane (g, col) of load j reads chunk col of row 4j + g; the rows then
         // pass through the wave's LDS tile into the MFMA operand layout.
@@ -662,7 +682,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int t = min(tc + 4 * j + g, t1 - 1);
-            int64_t blk = block_of(t, min(tc + 16 * (j >> 2), t1 - 1));
+            int64_t blk = block_of(tv, t, min(tc + 16 * (j >> 2), t1 - 1));
             if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
             kst[j] = v_stream(P.k_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col);
         }
@@ -675,7 +695,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         for (int hh = 0; hh < 2; ++hh) {
             const int tg = g + 4 * hh;
             const int t = min(tc + 4 * tg, t1 - 1);
-            int64_t blk = block_of(t, min(tc + 16 * hh, t1 - 1));
+            int64_t blk = block_of(tv, t, min(tc + 16 * hh, t1 - 1));
             if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
             const uint4* vp = P.v_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col;
             if (tc + 4 * tg + 3 < t1) {
@@ -1051,6 +1071,7 @@ hipError_t launch_prep(const StepArgs& a, bool with_append) {
     p.max_context_len = a.max_context_len;
     p.span = prefill_span(G);
     p.gp = decode_group_parts(G, a.head_dim);
+    p.dpart = decode_part(a.head_dim);
     p.cap_dec = a.lay.cap_dec;
     p.cap_pre = a.lay.cap_pre;
     p.hdr = (int32_t*)(ws + a.lay.hdr);

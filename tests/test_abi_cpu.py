@@ -127,6 +127,8 @@ def test_noalloc_scratch_limit_matches_the_header(kvc):
     m = re.search(r"#define KVC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m, "KVC_NOALLOC_SCRATCH_BYTES not found in kvc.h"
     assert kvc.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
-    # the headline mixed step (43 MB) fits; a 256-sequence MQA batch at 32K does not
+    # the headline mixed step (17 MB) and a 256-sequence MQA batch at 32K (38 MB)
+    # fit; 1024 sequences at 128K over 32 q heads (546 MB of partials) do not
     assert kvc.kvc_workspace_size(516, 2560, 512, 4096, 32, 8, 128, 16) <= kvc.NOALLOC_SCRATCH_BYTES
-    assert kvc.kvc_workspace_size(256, 256, 1, 32768, 32, 1, 128, 16) > kvc.NOALLOC_SCRATCH_BYTES
+    assert kvc.kvc_workspace_size(256, 256, 1, 32768, 32, 1, 128, 16) <= kvc.NOALLOC_SCRATCH_BYTES
+    assert kvc.kvc_workspace_size(1024, 1024, 1, 131071, 32, 1, 128, 16) > kvc.NOALLOC_SCRATCH_BYTES

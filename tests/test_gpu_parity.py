@@ -32,7 +32,11 @@ def _case(kvc, orc, name, specs, hq, hkv, a, bs, seed=7, scale=None):
     return compare(g, r, what=name)
 
 
-DEC_LENS = [0, 1, 5, 15, 16, 17, 255, 256, 257, 511, 512, 600, 1500]
+# decode edges: blocks (4, 16), the 256-token partitions of the vector-ALU
+# decode, and for head_dim 128 the 1024-token wave share and 4096-token work
+# item (a sequence of L = c + 1 tokens has ceil(L / 4096) items)
+DEC_LENS = [0, 1, 5, 15, 16, 17, 255, 256, 257, 511, 512, 600, 1500, 1023, 1024, 1025, 4095,
+            4096, 4097, 8200]
 PRE_SPECS = [(0, 2), (0, 63), (0, 64), (0, 65), (5, 130), (300, 200), (17, 1)]
 MIXED_SPECS = [(10, 0), (0, 1), (17, 5), (64, 1), (0, 0), (129, 77), (3000, 1), (0, 300),
                (700, 2), (255, 1), (1024, 129)]

@@ -2,7 +2,7 @@
 decode rows, prompt chunks and empty rows, over the supported head groupings
 (G = 1, 2 or a multiple of 4), block sizes 4 and 16 and head dims 16, 64, 128
 and 256,
-with context lengths drawn around block, tile and partition boundaries.  Same
+with context lengths drawn around block, tile, partition and work-item boundaries.  Same
 bar as the other parity tests (max |diff| <= 2e-2, mean <= 2e-3); the pools
 after the call equal the oracle's bit for bit."""
 import numpy as np
@@ -15,8 +15,10 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 24
 # context lengths near the edges the kernels care about: blocks (4, 16),
-# prefill key tiles (64), decode partitions (256)
-EDGES = [0, 1, 3, 4, 5, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513]
+# prefill key tiles (64), decode partitions (256; 1024 per wave and 4096 per
+# work item for head_dim 128)
+EDGES = [0, 1, 3, 4, 5, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025,
+         4095, 4096, 4097]
 
 
 def _case(i, dims=None):

@@ -72,11 +72,11 @@ def test_noalloc_equals_workspace_entry_two_calls(kvc, orc):
 
 
 def test_noalloc_refuses_a_step_beyond_the_scratch(kvc):
-    """256 sequences with contexts up to 32768 over 32 q heads need about
-    141 MB of split-K partials, more than the static array: refused with
+    """1024 sequences with contexts up to 131071 over 32 q heads need about
+    546 MB of split-K partials, more than the static array: refused with
     KVC_ERR_WORKSPACE, nothing launched (the output keeps its contents)."""
-    s, hq, hkv, a, bs = 256, 32, 1, 128, 16
-    need = kvc.kvc_workspace_size(s, s, 1, 32768, hq, hkv, a, bs)
+    s, hq, hkv, a, bs = 1024, 32, 1, 128, 16
+    need = kvc.kvc_workspace_size(s, s, 1, 131071, hq, hkv, a, bs)
     assert need > kvc.NOALLOC_SCRATCH_BYTES
     q = torch.zeros(s, hq, a, dtype=torch.bfloat16, device="cuda")
     out = torch.full_like(q, 3.0)
@@ -86,7 +86,7 @@ def test_noalloc_refuses_a_step_beyond_the_scratch(kvc):
     ctx = torch.zeros(s, dtype=torch.int32, device="cuda")
     with pytest.raises(kvc.KvcError) as ei:
         kvc.kvc_paged_attention_varlen_noalloc(out, q, None, None, cache, cache, table, cu, ctx,
-                                               0.1, max_q_len=1, max_context_len=32768)
+                                               0.1, max_q_len=1, max_context_len=131071)
     assert ei.value.status == kvc.KVC_ERR_WORKSPACE
     assert "static scratch" in str(ei.value)
     torch.cuda.synchronize()

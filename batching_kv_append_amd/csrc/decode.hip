@@ -667,18 +667,23 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         return __builtin_bit_cast(uint4, __builtin_nontemporal_load(
             reinterpret_cast<const u32x4_t*>(ptr)));
     };
-    for (int tc = t0; tc < t1; tc += STEP) {
-        int tv = tbl[0];  // the table register of this step (a uniform choice)
-        {
-            const int sel = ((tc - t0) / BS) >> 6;
+    // The table register that holds the entries of the step at tc (a uniform
+    // choice).  A step at or past t1 reads only token t1 - 1 (every token is
+    // clamped to it), so it takes that token's register.
+    auto table_reg = [&](int tc) -> int {
+        int tv = tbl[0];
+        const int sel = ((min(tc, t1 - 1) - t0) / BS) >> 6;
 #pragma unroll
-            for (int v = 1; v < NTV; ++v)
-                if (sel == v) tv = tbl[v];
-        }
-        // ---- K: 32 rows, four per load, each row whole (16 lanes x 16 B) --
-        // Lane (g, col) of load j reads chunk col of row 4j + g; the rows then
-        // pass through the wave's LDS tile into the MFMA operand layout.
-        uint4 kst[8];
+        for (int v = 1; v < NTV; ++v)
+            if (sel == v) tv = tbl[v];
+        return tv;
+    };
+    // ---- K: 32 rows, four per load, each row whole (16 lanes x 16 B) --
+    // Lane (g, col) of load j reads chunk col of row 4j + g; the rows then
+    // pass through the wave's LDS tile into the MFMA operand layout.
+    uint4 kst[8];
+    auto load_k = [&](int tc) __attribute__((always_inline)) {
+        const int tv = table_reg(tc);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int t = min(tc + 4 * j + g, t1 - 1);
@@ -686,11 +691,15 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
             kst[j] = v_stream(P.k_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col);
         }
-        // ---- V: token groups g and g+4 (4 tokens each) x chunk col --------
-        // Each load instruction reads four whole 256-byte rows.  Both
-        // branches load through the same helper, since merging a
-        // non-temporal load with a plain one drops the hint.
-        uint4 vb[2][4];
+    };
+    // ---- V: token groups g and g+4 (4 tokens each) x chunk col --------
+    // Each load instruction reads four whole 256-byte rows; rows past the
+    // end repeat the last row (their weight is 0).  No branch: the two sides
+    // of one would load into the same registers, and the second side would
+    // wait for every load in flight.
+    uint4 vb[2][4];
+    auto load_v = [&](int tc) __attribute__((always_inline)) {
+        const int tv = table_reg(tc);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int tg = g + 4 * hh;
@@ -698,14 +707,29 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             int64_t blk = block_of(tv, t, min(tc + 16 * hh, t1 - 1));
             if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
             const uint4* vp = P.v_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col;
-            if (tc + 4 * tg + 3 < t1) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) vb[hh][j] = v_stream(vp + j * CPR);
-            } else {  // rows past the end repeat the last row (their weight is 0)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    vb[hh][j] = v_stream(vp + (min(tc + 4 * tg + j, t1 - 1) - t) * CPR);
-            }
+            for (int j = 0; j < 4; ++j)
+                vb[hh][j] = v_stream(vp + (min(tc + 4 * tg + j, t1 - 1) - t) * CPR);
+        }
+    };
+    // With two head groups (PF) the next step's K rows are requested as soon
+    // as this step's are in LDS and the K operands in registers, and its V
+    // rows as soon as this step's V^T is in LDS, so they are in flight during
+    // this step's products and softmax (the load registers are free by then,
+    // and the kernel already runs two waves per SIMD).
+    constexpr bool PF = NG == 2;
+    if (PF) {
+        load_k(t0);
+        load_v(t0);
+    }
+    for (int tc = t0; tc < t1; tc += STEP) {
+        // The next step's loads are issued unconditionally, so every path has
+        // the same loads in flight and the waits stay partial; past the end
+        // every lane reads row t1 - 1 (one row, then unused).
+        const int tc_next = tc + STEP;
+        if (!PF) {
+            load_k(tc);
+            load_v(tc);
         }
         const bool padded = MASKED && tc < kstart;  // some key of this step is padding
         if (padded) {
@@ -733,6 +757,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
                 const int r = 16 * b + col;
                 kb[b][ks] = vt[r * 16 + ((4 * ks + g) ^ (r & 15))];
             }
+        if (PF) load_k(tc_next);
 
         // ---- S^T for the two blocks, per head group ---------------------------
         f32x4_t sc[NG][2];
@@ -768,6 +793,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
                 vt2[(d * 4 + (g ^ ((d >> 2) & 3))) * 2 + hh] = make_uint2(t01[e], t23[e]);
             }
         }
+        if (PF) load_v(tc_next);
 
         // ---- online softmax of this lane's column, per head group ------------
         const bool tail = tc + STEP > t1;

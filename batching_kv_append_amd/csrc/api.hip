@@ -493,6 +493,11 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
     const bool has_decode =
         max_q_len < 2 ||
         (int64_t)num_seqs * max_q_len - total_q >= (int64_t)max_q_len - 1;
+    // Chunks-only calls take the 8-wave prefill workgroups (one per compute
+    // unit, every K/V tile shared by 8 waves, P.V a tile late on half of
+    // them); beside a decode the 4-wave ones, which leave the decode more of
+    // each compute unit.
+    a.prefill_waves = (!has_decode && head_dim <= 128) ? 8 : 4;
 
     return run_step(a, has_decode, overlap, fn);
 }

@@ -1095,7 +1095,7 @@ hipError_t launch_prep(const StepArgs& a, bool with_append) {
     p.total_q = a.total_q;
     p.max_q_len = a.max_q_len;
     p.max_context_len = a.max_context_len;
-    p.span = prefill_span(G);
+    p.span = prefill_span(G, a.prefill_waves);
     p.gp = decode_group_parts(G, a.head_dim);
     p.dpart = decode_part(a.head_dim);
     p.cap_dec = a.lay.cap_dec;

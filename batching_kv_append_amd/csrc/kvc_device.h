@@ -39,7 +39,8 @@ constexpr int decode_part(int head_dim) {
 }
 
 // Prefill: each wave owns one query head and QW consecutive positions; a
-// workgroup of 4 waves covers HPW heads x (4/HPW) position blocks.
+// workgroup of NW waves (4, or 8 on calls without decode rows) covers HPW
+// heads x (NW/HPW) position blocks.
 constexpr int PREFILL_QW = 32;
 constexpr int PREFILL_TK = 64;  // keys per LDS tile
 
@@ -52,7 +53,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Prefill heads per workgroup for a group ratio G (G <= 4 divides 4, or G % 4 == 0).
 inline int prefill_hpw(int G) { return G >= 4 ? 4 : G; }
-inline int prefill_span(int G) { return PREFILL_QW * (4 / prefill_hpw(G)); }
+inline int prefill_span(int G, int nw = 4) { return PREFILL_QW * (nw / prefill_hpw(G)); }
 
 // Decode partitions per work item: the matrix decode (head_dim 128) cuts a
 // sequence into ceil(L / (4 * DECODE_PART_MFMA)) equal items, gives each of a
@@ -73,7 +74,7 @@ inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context
     const int64_t parts = ((int64_t)max_context_len + 1 + dp - 1) / dp;
     const int gp = decode_group_parts(G, head_dim);
     w.cap_dec = (int64_t)num_seqs * ((parts + gp - 1) / gp);
-    w.cap_pre = (int64_t)total_q / prefill_span(G) + num_seqs;
+    w.cap_pre = (int64_t)total_q / prefill_span(G) + num_seqs;  // 4-wave span: the most items
     size_t off = 0;
     w.hdr = off;        off = align_up(off + HDR_WORDS * 4, 256);
     w.dec_items = off;  off = align_up(off + (size_t)w.cap_dec * 8, 256);

@@ -21,18 +21,26 @@
 // numerator and the denominator share it, so the result is unchanged and the
 // accumulator rescale is rare.
 //
-// Work: one workgroup = 4 waves = HPW query heads of one kv group x (4/HPW)
-// blocks of QW = 32 positions; each wave owns one (head, 32 positions).  K/V
+// Work: one workgroup = NW waves = HPW query heads of one kv group x (NW/HPW)
+// blocks of QW = 32 positions; each wave owns one (head, 32 positions).  A
+// call with decode rows takes NW = 4: two workgroups per compute unit, which
+// leaves the co-running decode more of each unit.  A call of chunks only
+// takes NW = 8 up to head_dim 128: one workgroup per compute unit, two waves
+// per SIMD, so every K/V tile brought into the unit feeds 8 waves instead of
+// 4, and waves 4..7 (the second wave of each SIMD) run P.V one tile late, so
+// the two waves of a SIMD are out of phase (about 5 % on a 32K prompt).  K/V
 // tiles of 64 keys (gathered block by block through the block table) are
-// staged in LDS, double-buffered, once per workgroup and shared by the HPW
-// heads of the group (GQA, e2hang/Notes "MQA与GQA").  K and V are both stored
+// staged in LDS once per workgroup and shared by the HPW heads of the group
+// (GQA, e2hang/Notes "MQA与GQA"): K double-buffered, V in two buffers (four
+// with the late waves).  K and V are both stored
 // row-major, as they sit in the cache, each with its own 16-byte XOR swizzle:
 // the K operand is one ds_read_b128 per lane, and the V^T operand is read
 // with the transposing LDS load of gfx950 (ds_read_b64_tr_b16: within each
 // 16-lane group, lane o receives element o % 4 of the 8-byte loads of lanes
 // 4j + o / 4, j = 0..3), two per MFMA, so no transpose is done by the ALUs.
-// Each loading thread owns 4 consecutive keys x 8 dims and writes them with
-// 16-byte stores.  The planning kernel lists the workgroups costliest first.
+// Each loading thread owns KPT (1, 2 or 4) consecutive keys x 8 dims (twice
+// for head_dim 256) and writes them with 16-byte stores.  The planning kernel
+// lists the workgroups costliest first.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -96,9 +104,10 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
 // 0, 6, 10, 12 for row % 4 = 0..3, and 8 more when row % 16 >= 8.  A
 // transposing read takes 4 consecutive rows x 2 (16 lanes) or 4 (32 lanes)
 // consecutive chunks; bits 1-2 and bits 2-3 of the four swizzles are both
-// all distinct, so either lane group hits distinct banks.  16-byte row
-// writes by the tile loaders (8 chunks of rows k and k + 8 per 16 lanes) are
-// conflict-free as well.
+// all distinct, so either lane group hits distinct banks.  The tile loaders'
+// 16-byte writes (16 lanes: the 16 chunks of one row, or with head_dim 64
+// the 8 chunks of two adjacent rows) are conflict-free as well: the swizzle
+// permutes the chunks within a row.
 template <int CPR>
 __device__ __forceinline__ int vswz(int row) {
     return (((row & 1) * 6) ^ (((row >> 1) & 1) * 10) ^ (row & 8)) & (CPR - 1);
@@ -126,26 +135,34 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)const_cast<char*>(p));
 }
 
-// head_dim 256 doubles the accumulators and the Q^T operand: one workgroup
-// (128 KiB of LDS) per compute unit.
-template <int A, int BS, int HPW>
-__global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillParams P) {
+// NW = 4: two workgroups per compute unit (one for head_dim 256, whose
+// accumulators and Q^T operand double: 128 KiB of LDS, one wave per SIMD).
+// NW = 8 (calls without decode rows, head_dim <= 128): one workgroup per
+// compute unit, two waves per SIMD, each K/V tile fetched once for 8 waves,
+// and the second wave of each SIMD runs P.V one tile late.
+template <int A, int BS, int HPW, int NW>
+__global__ __launch_bounds__(64 * NW, A > 128 ? 1 : 2) void prefill_kernel(PrefillParams P) {
+    static_assert(NW == 4 || (NW == 8 && A <= 128), "8-wave workgroups up to head_dim 128");
+    constexpr int NT = 64 * NW;            // threads per workgroup
     constexpr int TK = PREFILL_TK;         // keys per tile (64)
     constexpr int CPR = A / 8;             // 16-byte chunks per K/V row
     constexpr int KK = A / 16;             // 16-dim MFMA steps of QK^T
     constexpr int DT = (A + 31) / 32;      // 32-dim output tiles
     constexpr int QW = PREFILL_QW;         // positions per wave (32)
-    constexpr int SPAN = QW * (4 / HPW);   // positions per workgroup
-    constexpr int KGC = (TK / 4) * CPR;    // (4-key group, 16-byte chunk) loads of a tile
-    constexpr int NKC = (KGC + 255) / 256; // of them per thread (2 for head_dim 256)
-    constexpr int LOADERS = KGC < 256 ? KGC : 256;  // threads that load
+    constexpr int SPAN = QW * (NW / HPW);  // positions per workgroup
+    constexpr int CW = CPR < 16 ? CPR : 16;  // loading threads along one row
+    constexpr int NKC = CPR / CW;          // 16-byte chunks per thread and row (2 for head_dim 256)
+    constexpr int KPT = TK * CW / NT > 0 ? TK * CW / NT : 1;  // keys per loading thread
+    constexpr int LOADERS = (TK / KPT) * CW;  // threads that load
     constexpr float NEG_BIG = -1.0e30f;
     constexpr float RESCALE_SLACK = 8.0f;  // log2 units: weights stay < 2^8
-    static_assert(KGC == LOADERS * NKC, "tile loaders");
-    static_assert(BS % 4 == 0, "4 consecutive keys must share a block");
+    static_assert(LOADERS <= NT && LOADERS * KPT * NKC == TK * CPR, "tile loaders");
+    static_assert(BS % KPT == 0, "a thread's keys must share a block");
 
     __shared__ uint4 sK[2][TK * CPR];  // [key][chunk ^ (key % CPR)]
-    __shared__ uint4 sV[2][TK * CPR];  // [key][chunk ^ vswz(key)]
+    constexpr int NVB = NW == 8 ? 4 : 2;  // V tiles in LDS (four: P.V runs a tile late on half the waves)
+    __shared__ uint4 sV[NVB][TK * CPR];  // [key][chunk ^ vswz(key)]
+    __shared__ int sTab[2][TK / BS];   // block ids of the next tile's blocks
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -193,42 +210,40 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
     float m = NEG_BIG;  // running maximum, scaled log2 units
     float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // partial denominators, one per 16-key step
 
-    // ---- cooperative tile loads: thread = 4 consecutive keys x one chunk ----
-    // The 4 keys of a group share one cache block (k0 and 4 kg are multiples
-    // of 4, and so is the block size), so a thread reads 4 rows of one block
-    // at fixed offsets.  A group at or past L reads the rows of the block
+    // ---- cooperative tile loads: thread = KPT consecutive keys x one chunk ---
+    // The KPT keys of a thread share one cache block (k0 and its first key
+    // are multiples of KPT, and so is the block size), so a thread reads KPT
+    // rows of one block at fixed offsets.  A group at or past L reads the rows of the block
     // that holds key L-1 instead (memory of that block, whatever it holds):
     // keys >= L are masked out of every stored row's scores by select, and
     // their V rows are zeroed before they reach LDS, so their weight of 0
     // never meets a non-finite value.
-    const bool loader = tid < LOADERS;
-    // Thread -> (key group kg: keys 4kg .. 4kg+3, 16-byte chunk cc: dims
-    // 8cc .. 8cc+7; with head_dim 256 also chunk cc + 16).  Wave w covers key
-    // groups 4w .. 4w+3.  For A >= 128 each 16-lane group holds chunks
-    // 8h .. 8h+7 of key groups kg and kg ^ 2, so its 16-byte stores (one row
-    // per store) hit 16 distinct bank groups.
-    int kg, cc;
-    if constexpr (CPR >= 16) {
-        kg = ((tid >> 5) & 1) | (((tid >> 3) & 1) << 1) | ((tid >> 6) << 2);
-        cc = (tid & 7) | (((tid >> 4) & 1) << 3);
-    } else {
-        kg = tid / CPR;
-        cc = tid % CPR;
-    }
+    const bool loader = LOADERS == NT || tid < LOADERS;  // a constant when every thread loads
+    // Thread -> (keys kb .. kb+KPT-1, 16-byte chunk cc: dims 8cc .. 8cc+7;
+    // with head_dim 256 also chunk cc + 16).  The CW threads of a row are
+    // consecutive lanes, so a 16-byte store instruction writes whole rows
+    // (16 distinct bank groups per row with the swizzles below) and a load
+    // instruction reads whole 256-byte row segments.
+    const int cc = tid % CW;
+    const int kb = KPT * (tid / CW);
     // offset (16-byte units) of the thread's first row inside a cache block
-    const uint32_t toff = (uint32_t)((kvh * BS + (4 * kg) % BS) * CPR + cc);
+    const uint32_t toff = (uint32_t)((kvh * BS + kb % BS) * CPR + cc);
     const uint32_t blk_stride = (uint32_t)(P.hkv * BS * CPR);
-    u32x4_t kreg[4 * NKC], vreg[4 * NKC];  // native vectors: the staging stays in VGPRs
+    u32x4_t kreg[KPT * NKC], vreg[KPT * NKC];  // native vectors: the staging stays in VGPRs
     int bad = 0;
-    // Block-table entry of this thread's key group in the tile at k0 (-1 past
-    // the table).  Read one tile ahead of its use, so the K/V addresses never
-    // wait for the table.
+    // Block-table entry of this thread's keys in the tile at k0 (tiles past
+    // the end give the block of key L-1).  Entries are read two tiles ahead,
+    // unconditionally (an index past the row is clamped into it and flagged),
+    // and handed on through LDS: every thread publishes the entry of its
+    // block with the tile's stores (the threads of one block compute the
+    // same entry), and the next step reads it from there.  So no register
+    // carries a global load across the loop, and no step waits for the table.
+    const int kblk = loader ? kb / BS : 0;  // the thread's block within a tile
     int short_tbl = 0;  // a needed block is past the table row
     auto table_entry = [&](int k0) __attribute__((always_inline)) -> int {
-        const int lb = min(k0 + 4 * kg, L - 1) / BS;
-        if (lb < P.max_blocks) return P.table[(int64_t)s * P.max_blocks + lb];
-        short_tbl = 1;
-        return 0;  // in range; the result is flagged
+        const int lb = min(k0 + kb, L - 1) / BS;
+        short_tbl |= lb >= P.max_blocks;
+        return P.table[(int64_t)s * P.max_blocks + min(lb, P.max_blocks - 1)];
     };
     auto load_tile = [&](int entry) __attribute__((always_inline)) {
         if (!loader) return;
@@ -243,28 +258,28 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
 #pragma unroll
         for (int c = 0; c < NKC; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kreg[c * 4 + j] = __builtin_bit_cast(u32x4_t, kp[j * CPR + c * 16]);
-                vreg[c * 4 + j] = __builtin_bit_cast(u32x4_t, vp[j * CPR + c * 16]);
+            for (int j = 0; j < KPT; ++j) {
+                kreg[c * KPT + j] = __builtin_bit_cast(u32x4_t, kp[j * CPR + c * 16]);
+                vreg[c * KPT + j] = __builtin_bit_cast(u32x4_t, vp[j * CPR + c * 16]);
             }
     };
-    auto store_tile = [&](int buf, int k0) __attribute__((always_inline)) {
+    auto store_tile = [&](int kbuf, int vbuf, int k0) __attribute__((always_inline)) {
         if (!loader) return;
-        if (k0 + 4 * kg + 3 >= L) {  // the sequence's last keys: V rows past L are zero
+        if (k0 + kb + KPT - 1 >= L) {  // the sequence's last keys: V rows past L are zero
 #pragma unroll
             for (int c = 0; c < NKC; ++c)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (k0 + 4 * kg + j >= L) vreg[c * 4 + j] = u32x4_t{0u, 0u, 0u, 0u};
+                for (int j = 0; j < KPT; ++j)
+                    if (k0 + kb + j >= L) vreg[c * KPT + j] = u32x4_t{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int c = 0; c < NKC; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = 4 * kg + j;
+            for (int j = 0; j < KPT; ++j) {
+                const int key = kb + j;
                 const int ch = cc + c * 16;
-                sK[buf][key * CPR + (ch ^ (key % CPR))] = __builtin_bit_cast(uint4, kreg[c * 4 + j]);
-                sV[buf][key * CPR + (ch ^ vswz<CPR>(key))] = __builtin_bit_cast(uint4, vreg[c * 4 + j]);
+                sK[kbuf][key * CPR + (ch ^ (key % CPR))] = __builtin_bit_cast(uint4, kreg[c * KPT + j]);
+                sV[vbuf][key * CPR + (ch ^ vswz<CPR>(key))] = __builtin_bit_cast(uint4, vreg[c * KPT + j]);
             }
     };
     // Transposing-read offsets (bytes inside a V tile) of this lane for the
@@ -286,11 +301,13 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
             troff[dt][rd] = row * CPR * 16 + (chunk ^ vswz<CPR>(row)) * 16 + (q & 1) * 8;
         }
 
-    int entry_next = 0;  // table entry of the tile after the one being loaded
-    if (nkt > 0) {
-        load_tile(table_entry(0));
-        if (nkt > 1) entry_next = table_entry(TK);
-        store_tile(0, 0);
+    {
+        const int e1 = table_entry(TK);
+        if (nkt > 0) {
+            load_tile(table_entry(0));
+            store_tile(0, 0, 0);
+        }
+        if (loader) sTab[1][kblk] = e1;
     }
     __syncthreads();
     // Explicit wait for everything issued so far (the Q^T operand loads are
@@ -298,19 +315,18 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
     // flight inside the loop and waits for ALL loads, the next tile's
     // included, before the first MFMA of every tile).
     __builtin_amdgcn_s_waitcnt(0);
-    // One tile step; the buffer index is a compile-time constant (the loop
-    // below is unrolled by two), so every LDS address of a step is a per-lane
+    // With 8 waves, waves 4..7 (the second wave of each SIMD) run P.V one
+    // tile late: in step t they multiply the previous tile's weights by its V
+    // tile (kept in its own buffer: V tiles rotate through four), then take
+    // this tile's scores and softmax.  So the two waves of a SIMD are out of
+    // phase: one issues matrix work while the other does its vector work.
+    // Each tile step's buffer indices are compile-time constants (the loop
+    // is unrolled by four), so every LDS address of a step is a per-lane
     // register plus an immediate.
-    auto tile_step = [&](const int t, auto bufc) __attribute__((always_inline)) {
-        constexpr int buf = decltype(bufc)::value;
-        const int k0 = t * TK;
-        if (t + 1 < nkt) {  // in flight during this tile's math
-            const int entry = entry_next;
-            if (t + 2 < nkt) entry_next = table_entry(k0 + 2 * TK);
-            load_tile(entry);
-        }
-
-        if (k0 < kend_w) {
+    const bool late = NW == 8 && wave >= 4;
+    uint4 pb[2][2];  // [kh][ks] bf16 P^T operands
+    auto qk_soft = [&](const int k0, auto kbc) __attribute__((always_inline)) {
+        constexpr int kb_ = decltype(kbc)::value;
             // Raised wave priority around the two MFMA blocks: a wave that
             // reaches its matrix work is issued ahead of the others' softmax
             // and LDS stores, so the matrix pipe idles less (about 2% on long
@@ -328,7 +344,7 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
                 for (int kh = 0; kh < 2; ++kh) {
                     const int key = kh * 32 + col;
                     const int ch = kk * 2 + hi;
-                    const uint4 a = sK[buf][key * CPR + (ch ^ (key % CPR))];
+                    const uint4 a = sK[kb_][key * CPR + (ch ^ (key % CPR))];
                     sacc[kh] = mfma32(a, qreg[kk], sacc[kh]);
                 }
             }
@@ -376,7 +392,6 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
                     for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
             }
             const float mc = pos_scale ? cs : 1.f;
-            uint4 pb[2][2];  // [kh][ks] bf16 P^T operands
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 float p[16];
@@ -398,12 +413,15 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
                 }
             }
 
-            __builtin_amdgcn_s_setprio(2);
-            // ---- O^T += V^T P^T ---------------------------------------------
+    };
+    auto pv = [&](auto vbc) __attribute__((always_inline)) {
+        constexpr int vb_ = decltype(vbc)::value;
+        __builtin_amdgcn_s_setprio(2);
+        // ---- O^T += V^T P^T ---------------------------------------------
             // Operand slot e of lane l holds V[key][32 dt + l % 32] for key
             // 32 kh + 16 ks + 8 (e / 4) + 4 (l / 32) + e % 4, the key order of
             // the P^T slots.
-            const char* vb = reinterpret_cast<const char*>(&sV[buf][0]);
+            const char* vb = reinterpret_cast<const char*>(&sV[vb_][0]);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -418,16 +436,45 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
                         o[dt] = mfma32(__builtin_bit_cast(uint4, a8), pb[kh][ks], o[dt]);
                     }
             }
-        }
-
-        __builtin_amdgcn_s_setprio(0);
-        if (t + 1 < nkt) store_tile(buf ^ 1, k0 + TK);
-        __syncthreads();
     };
-    for (int t = 0; t < nkt; t += 2) {
-        tile_step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < nkt) tile_step(t + 1, std::integral_constant<int, 1>{});
-    }
+    auto run = [&](auto latec) __attribute__((always_inline)) {
+        constexpr bool LATE = decltype(latec)::value;
+        bool prev = false;  // the previous tile's weights wait for their P.V
+        auto tile_step = [&](const int t, auto bc) __attribute__((always_inline)) {
+            constexpr int b = decltype(bc)::value;  // t % 4
+            const int k0 = t * TK;
+            const int entry2 = table_entry(k0 + 2 * TK);           // consumed by this step's stores
+            if (t + 1 < nkt) load_tile(sTab[(b & 1) ^ 1][kblk]);  // in flight during this tile's math
+            if (LATE) {
+                if (prev) pv(std::integral_constant<int, (b + NVB - 1) % NVB>{});
+                prev = k0 < kend_w;
+                if (prev) qk_soft(k0, std::integral_constant<int, b & 1>{});
+            } else if (k0 < kend_w) {
+                qk_soft(k0, std::integral_constant<int, b & 1>{});
+                pv(std::integral_constant<int, b % NVB>{});
+            }
+            __builtin_amdgcn_s_setprio(0);
+            if (t + 1 < nkt) store_tile((b & 1) ^ 1, (b + 1) % NVB, k0 + TK);
+            if (loader) sTab[b & 1][kblk] = entry2;  // the tile after next
+            __syncthreads();
+        };
+        for (int t = 0; t < nkt; t += 4) {
+            tile_step(t, std::integral_constant<int, 0>{});
+            if (t + 1 < nkt) tile_step(t + 1, std::integral_constant<int, 1>{});
+            if (t + 2 < nkt) tile_step(t + 2, std::integral_constant<int, 2>{});
+            if (t + 3 < nkt) tile_step(t + 3, std::integral_constant<int, 3>{});
+        }
+        if (LATE && prev) {  // the last tile's P.V (its V tile is still in place)
+            switch ((nkt - 1) % NVB) {
+                case 0: pv(std::integral_constant<int, 0>{}); break;
+                case 1: pv(std::integral_constant<int, 1 % NVB>{}); break;
+                case 2: pv(std::integral_constant<int, 2 % NVB>{}); break;
+                default: pv(std::integral_constant<int, 3 % NVB>{}); break;
+            }
+        }
+    };
+    if (late) run(std::true_type{});
+    else run(std::false_type{});
     if (short_tbl) atomicOr(P.hdr + HDR_FLAGS, FLAG_TABLE_SHORT);
     if (bad) atomicOr(P.hdr + HDR_FLAGS, FLAG_BAD_BLOCK);
 
@@ -453,13 +500,25 @@ __global__ __launch_bounds__(256, A > 128 ? 1 : 2) void prefill_kernel(PrefillPa
     }
 }
 
+template <int A, int BS, int NW>
+void launch_prefill_nw(const StepArgs& a, const PrefillParams& p, int hpw, dim3 grid) {
+    const dim3 block(64 * NW);
+    switch (hpw) {
+        case 1: hipLaunchKernelGGL((prefill_kernel<A, BS, 1, NW>), grid, block, 0, a.stream, p); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<A, BS, 2, NW>), grid, block, 0, a.stream, p); break;
+        default: hipLaunchKernelGGL((prefill_kernel<A, BS, 4, NW>), grid, block, 0, a.stream, p); break;
+    }
+}
+
 template <int A, int BS>
 void launch_prefill_hpw(const StepArgs& a, const PrefillParams& p, int hpw, dim3 grid) {
-    switch (hpw) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<A, BS, 1>), grid, dim3(256), 0, a.stream, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<A, BS, 2>), grid, dim3(256), 0, a.stream, p); break;
-        default: hipLaunchKernelGGL((prefill_kernel<A, BS, 4>), grid, dim3(256), 0, a.stream, p); break;
+    if constexpr (A <= 128) {
+        if (a.prefill_waves == 8) {
+            launch_prefill_nw<A, BS, 8>(a, p, hpw, grid);
+            return;
+        }
     }
+    launch_prefill_nw<A, BS, 4>(a, p, hpw, grid);
 }
 
 }  // namespace

@@ -43,7 +43,8 @@ def _gather(wl, s, p):
     return wl.k_pool[blk, :, p % wl.block_size, :], wl.v_pool[blk, :, p % wl.block_size, :]
 
 
-@pytest.mark.parametrize("geom", [(32, 8, 16), (8, 2, 4), (32, 1, 16)], ids=["gqa4", "gqa4_bs4", "mqa"])
+@pytest.mark.parametrize("geom", [(32, 8, 16), (8, 2, 4), (32, 1, 16), (32, 1, 4)],
+                         ids=["gqa4", "gqa4_bs4", "mqa", "mqa_bs4"])
 def test_left_padded_batch_matches_the_ragged_oracle(kvc, orc, geom):
     hq, hkv, bs = geom
     wl = _ragged(hq, hkv, bs, seed=51)

@@ -38,6 +38,8 @@ def _case(kvc, orc, name, specs, hq, hkv, a, bs, seed=7, scale=None):
 DEC_LENS = [0, 1, 5, 15, 16, 17, 255, 256, 257, 511, 512, 600, 1500, 1023, 1024, 1025, 4095,
             4096, 4097, 8200]
 PRE_SPECS = [(0, 2), (0, 63), (0, 64), (0, 65), (5, 130), (300, 200), (17, 1)]
+# chunks of equal length: the host sizes rule decode rows out
+PRE_ONLY = [(0, 77), (5, 77), (63, 77), (64, 77), (300, 77), (1000, 77), (1500, 77)]
 MIXED_SPECS = [(10, 0), (0, 1), (17, 5), (64, 1), (0, 0), (129, 77), (3000, 1), (0, 300),
                (700, 2), (255, 1), (1024, 129)]
 SMALL = [
@@ -56,6 +58,16 @@ SMALL = [
     ("prefill_gqa4_bs4", PRE_SPECS, 8, 2, 128, 4),
     ("prefill_gqa8", PRE_SPECS, 8, 1, 128, 16),
     ("mixed_gqa4", MIXED_SPECS, 8, 2, 128, 16),
+    # chunks only (no decode row): the 8-wave prefill workgroups, P.V a tile
+    # late on half the waves, V tiles in four buffers (tile counts 2..25)
+    ("chunks_only_mha", PRE_ONLY, 2, 2, 128, 16),
+    ("chunks_only_gqa2_bs4", PRE_ONLY, 4, 2, 128, 4),
+    ("chunks_only_gqa4", PRE_ONLY, 8, 2, 128, 16),
+    ("chunks_only_g32", PRE_ONLY, 32, 1, 128, 16),
+    ("chunks_only_a64_gqa4_bs4", PRE_ONLY, 8, 2, 64, 4),
+    ("chunks_only_a16_gqa2", PRE_ONLY, 4, 2, 16, 16),
+    ("chunks_only_a256_gqa4", PRE_ONLY, 8, 2, 256, 16),
+    ("chunks_only_one_seq", [(2000, 131)], 8, 2, 128, 16),
     ("mixed_mha_bs4", MIXED_SPECS, 2, 2, 128, 4),
     ("a16_mixed", [(0, 7), (4, 3), (7, 1), (30, 1), (100, 40), (0, 1), (257, 1)], 1, 1, 16, 4),
     ("a16_gqa2_bs16", [(0, 7), (4, 3), (7, 1), (30, 1), (100, 40), (600, 1)], 4, 2, 16, 16),

@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     __shared__ float sML[GP][2][16 * NG];  // per wave: column max, column total
     __shared__ int arrived;                        // waves of the group done
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
     const int lane = threadIdx.x & 63;
     const int col = lane & 15;  // head column
     const int g = lane >> 4;    // token group: tokens 4g..4g+3 of each 16-token block
@@ -718,6 +718,10 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     // this step's products and softmax (the load registers are free by then,
     // and the kernel already runs two waves per SIMD).
     constexpr bool PF = NG == 2;
+    // Wait here for everything requested so far (the table slice and the Q^T
+    // operand, whose loads are conditional), so the loop's waits count only
+    // its own K/V loads and can leave the V rows in flight while K is used.
+    __builtin_amdgcn_s_waitcnt(0);
     if (PF) {
         load_k(t0);
         load_v(t0);

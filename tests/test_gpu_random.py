@@ -45,9 +45,27 @@ def _case(i, dims=None):
                 hkv=hkv, a=a, bs=bs, seed=2000 + i)
 
 
+def _chunks_only_case(i):
+    """Every sequence brings the same number of rows (>= 2), so the host sizes
+    rule decode rows out and the call takes the 8-wave prefill workgroups."""
+    rng = np.random.default_rng(3000 + i)
+    g = int(rng.choice([1, 2, 4, 8, 32]))
+    hkv = int(rng.choice([1, 2])) if g <= 8 else 1
+    a = int(rng.choice([16, 64, 128, 128]))
+    bs = int(rng.choice([4, 16]))
+    q = int(rng.integers(2, 200))
+    n = int(rng.integers(1, 7))
+    specs = [(int(rng.choice(EDGES)) if rng.random() < 0.5 else int(rng.integers(0, 3000)), q)
+             for _ in range(n)]
+    return dict(name=f"chunks{i:02d}_g{g}_hkv{hkv}_a{a}_bs{bs}_q{q}", specs=specs, hq=g * hkv,
+                hkv=hkv, a=a, bs=bs, seed=4000 + i)
+
+
 CASES = [_case(i) for i in range(N_CASES)]
 # head dims 64 and 256 (the vector-ALU decode and the prefill instances of those sizes)
 CASES += [_case(i, dims=(64, 256)) for i in range(N_CASES, N_CASES + 12)]
+# chunks only (the 8-wave prefill with P.V a tile late on half the waves)
+CASES += [_chunks_only_case(i) for i in range(10)]
 
 
 @pytest.fixture(scope="module")

@@ -959,8 +959,8 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
 
 // ---------------------------------------------------------------------------
 // Merge kernel: one wave per (decode sequence with several work items, query
-// head); a work item's partial covers one partition group (or one partition
-// on the head_dim 16 path).
+// head); a work item's partial covers one partition group (one partition on
+// the vector-ALU path of head_dims 16, 64 and 256).
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // The plan's descriptor carries everything the wave needs, and the (m, l)
 // pairs and accumulators of up to 32 partials are requested together, so a

@@ -58,8 +58,8 @@ inline int prefill_span(int G, int nw = 4) { return PREFILL_QW * (nw / prefill_h
 // Decode partitions per work item: the matrix decode (head_dim 128) cuts a
 // sequence into ceil(L / (4 * DECODE_PART_MFMA)) equal items, gives each of a
 // workgroup's four waves a quarter of one item and combines them in LDS, so
-// split-K partials exist per item; the head_dim 16 decode takes one partition
-// per wave.
+// split-K partials exist per item; the vector-ALU decode (head_dims 16, 64
+// and 256) takes one partition per wave.
 constexpr int DECODE_GROUP = 4;  // partitions per matrix-decode workgroup (its four waves)
 inline int decode_group_parts(int G, int head_dim) {
     (void)G;

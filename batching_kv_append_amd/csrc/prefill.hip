@@ -213,8 +213,9 @@ __global__ __launch_bounds__(64 * NW, A > 128 ? 1 : 2) void prefill_kernel(Prefi
     // ---- cooperative tile loads: thread = KPT consecutive keys x one chunk ---
     // The KPT keys of a thread share one cache block (k0 and its first key
     // are multiples of KPT, and so is the block size), so a thread reads KPT
-    // rows of one block at fixed offsets.  A group at or past L reads the rows of the block
-    // that holds key L-1 instead (memory of that block, whatever it holds):
+    // rows of one block at fixed offsets.  A thread whose keys are at or past L
+    // reads the rows of the block that holds key L-1 instead (memory of that
+    // block, whatever it holds):
     // keys >= L are masked out of every stored row's scores by select, and
     // their V rows are zeroed before they reach LDS, so their weight of 0
     // never meets a non-finite value.
@@ -326,116 +327,116 @@ __global__ __launch_bounds__(64 * NW, A > 128 ? 1 : 2) void prefill_kernel(Prefi
     const bool late = NW == 8 && wave >= 4;
     uint4 pb[2][2];  // [kh][ks] bf16 P^T operands
     auto qk_soft = [&](const int k0, auto kbc) __attribute__((always_inline)) {
-        constexpr int kb_ = decltype(kbc)::value;
-            // Raised wave priority around the two MFMA blocks: a wave that
-            // reaches its matrix work is issued ahead of the others' softmax
-            // and LDS stores, so the matrix pipe idles less (about 2% on long
-            // chunks).
-            __builtin_amdgcn_s_setprio(2);
-            // ---- S^T = K Q^T : two 32-key halves -------------------------
-            f32x16_t sacc[2];
+        constexpr int kbuf = decltype(kbc)::value;  // K tile buffer
+        // Raised wave priority around the two MFMA blocks: a wave that
+        // reaches its matrix work is issued ahead of the others' softmax
+        // and LDS stores, so the matrix pipe idles less (about 2% on long
+        // chunks).
+        __builtin_amdgcn_s_setprio(2);
+        // ---- S^T = K Q^T : two 32-key halves -------------------------
+        f32x16_t sacc[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kh][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const int key = kh * 32 + col;
+                const int ch = kk * 2 + hi;
+                const uint4 a = sK[kbuf][key * CPR + (ch ^ (key % CPR))];
+                sacc[kh] = mfma32(a, qreg[kk], sacc[kh]);
+            }
+        }
+
+        __builtin_amdgcn_s_setprio(0);
+        // ---- online softmax of this lane's column ---------------------
+        const int lim = c + p0 + col;               // last visible key of the column
+        const bool diag = k0 + TK - 1 > c + p0;     // some key may be masked
+        if (!pos_scale) {
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kh][r] = 0.f;
+                for (int r = 0; r < 16; ++r) sacc[kh][r] *= cs;
+        }
+        if (diag) {
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    const int key = kh * 32 + col;
-                    const int ch = kk * 2 + hi;
-                    const uint4 a = sK[kb_][key * CPR + (ch ^ (key % CPR))];
-                    sacc[kh] = mfma32(a, qreg[kk], sacc[kh]);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kh * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (key > lim) sacc[kh][r] = -INFINITY;
                 }
+        }
+        // column maximum: four independent chains, then the other half-wave
+        float mq[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mq[i] = fmaxf(sacc[i >> 1][(i & 1) * 8], sacc[i >> 1][(i & 1) * 8 + 1]);
+#pragma unroll
+            for (int r = 2; r < 8; ++r) mq[i] = fmaxf(mq[i], sacc[i >> 1][(i & 1) * 8 + r]);
+        }
+        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+        mx = halves_max(mx);
+        const float cand = pos_scale ? mx * cs : mx;  // column max, scaled log2 units
+        const bool grow = cand > m + RESCALE_SLACK;
+        if (__any(grow)) {
+            const float m_new = grow ? cand : m;
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            m = m_new;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
+        const float mc = pos_scale ? cs : 1.f;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][r], mc, -m));
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                pb[kh][ks].x = pack_bf16x2(p[ks * 8 + 0], p[ks * 8 + 1]);
+                pb[kh][ks].y = pack_bf16x2(p[ks * 8 + 2], p[ks * 8 + 3]);
+                pb[kh][ks].z = pack_bf16x2(p[ks * 8 + 4], p[ks * 8 + 5]);
+                pb[kh][ks].w = pack_bf16x2(p[ks * 8 + 6], p[ks * 8 + 7]);
+                // the denominator sums the same bf16 weights the P.V
+                // product uses: one dot2 with (1, 1) per pair
+                float& ls = lsum[kh * 2 + ks];
+                ls = sum_bf16x2(pb[kh][ks].x, ls);
+                ls = sum_bf16x2(pb[kh][ks].y, ls);
+                ls = sum_bf16x2(pb[kh][ks].z, ls);
+                ls = sum_bf16x2(pb[kh][ks].w, ls);
             }
-
-            __builtin_amdgcn_s_setprio(0);
-            // ---- online softmax of this lane's column ---------------------
-            const int lim = c + p0 + col;               // last visible key of the column
-            const bool diag = k0 + TK - 1 > c + p0;     // some key may be masked
-            if (!pos_scale) {
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[kh][r] *= cs;
-            }
-            if (diag) {
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kh * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if (key > lim) sacc[kh][r] = -INFINITY;
-                    }
-            }
-            // column maximum: four independent chains, then the other half-wave
-            float mq[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                mq[i] = fmaxf(sacc[i >> 1][(i & 1) * 8], sacc[i >> 1][(i & 1) * 8 + 1]);
-#pragma unroll
-                for (int r = 2; r < 8; ++r) mq[i] = fmaxf(mq[i], sacc[i >> 1][(i & 1) * 8 + r]);
-            }
-            float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-            mx = halves_max(mx);
-            const float cand = pos_scale ? mx * cs : mx;  // column max, scaled log2 units
-            const bool grow = cand > m + RESCALE_SLACK;
-            if (__any(grow)) {
-                const float m_new = grow ? cand : m;
-                const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-                m = m_new;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            }
-            const float mc = pos_scale ? cs : 1.f;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                float p[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kh][r], mc, -m));
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    pb[kh][ks].x = pack_bf16x2(p[ks * 8 + 0], p[ks * 8 + 1]);
-                    pb[kh][ks].y = pack_bf16x2(p[ks * 8 + 2], p[ks * 8 + 3]);
-                    pb[kh][ks].z = pack_bf16x2(p[ks * 8 + 4], p[ks * 8 + 5]);
-                    pb[kh][ks].w = pack_bf16x2(p[ks * 8 + 6], p[ks * 8 + 7]);
-                    // the denominator sums the same bf16 weights the P.V
-                    // product uses: one dot2 with (1, 1) per pair
-                    float& ls = lsum[kh * 2 + ks];
-                    ls = sum_bf16x2(pb[kh][ks].x, ls);
-                    ls = sum_bf16x2(pb[kh][ks].y, ls);
-                    ls = sum_bf16x2(pb[kh][ks].z, ls);
-                    ls = sum_bf16x2(pb[kh][ks].w, ls);
-                }
-            }
+        }
 
     };
     auto pv = [&](auto vbc) __attribute__((always_inline)) {
-        constexpr int vb_ = decltype(vbc)::value;
+        constexpr int vbuf = decltype(vbc)::value;  // V tile buffer
         __builtin_amdgcn_s_setprio(2);
         // ---- O^T += V^T P^T ---------------------------------------------
-            // Operand slot e of lane l holds V[key][32 dt + l % 32] for key
-            // 32 kh + 16 ks + 8 (e / 4) + 4 (l / 32) + e % 4, the key order of
-            // the P^T slots.
-            const char* vb = reinterpret_cast<const char*>(&sV[vb_][0]);
+        // Operand slot e of lane l holds V[key][32 dt + l % 32] for key
+        // 32 kh + 16 ks + 8 (e / 4) + 4 (l / 32) + e % 4, the key order of
+        // the P^T slots.
+        const char* vb = reinterpret_cast<const char*>(&sV[vbuf][0]);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
+        for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        const int rb = (kh * 32 + ks * 16) * CPR * 16;
-                        const i16x4_t v0 = lds_read_tr16(vb + troff[dt][0] + rb);
-                        const i16x4_t v1 = lds_read_tr16(vb + troff[dt][1] + rb);
-                        i16x8_t a8 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        if (A < 32 && (lane & 16)) a8 = i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-                        o[dt] = mfma32(__builtin_bit_cast(uint4, a8), pb[kh][ks], o[dt]);
-                    }
-            }
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int rb = (kh * 32 + ks * 16) * CPR * 16;
+                    const i16x4_t v0 = lds_read_tr16(vb + troff[dt][0] + rb);
+                    const i16x4_t v1 = lds_read_tr16(vb + troff[dt][1] + rb);
+                    i16x8_t a8 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    if (A < 32 && (lane & 16)) a8 = i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                    o[dt] = mfma32(__builtin_bit_cast(uint4, a8), pb[kh][ks], o[dt]);
+                }
+        }
     };
     auto run = [&](auto latec) __attribute__((always_inline)) {
         constexpr bool LATE = decltype(latec)::value;

@@ -720,7 +720,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     constexpr bool PF = NG == 2;
     // Wait here for everything requested so far (the table slice and the Q^T
     // operand, whose loads are conditional), so the loop's waits count only
-    // its own K/V loads and can leave the V rows in flight while K is used.
+    // its own K/V loads.
     __builtin_amdgcn_s_waitcnt(0);
     if (PF) {
         load_k(t0);

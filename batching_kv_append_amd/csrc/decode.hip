@@ -244,7 +244,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     const int npre = (int)min((int64_t)carry[1], cap_pre);
     auto bucket_of = [&](int2 item) {
         const int q = cu[item.x + 1] - cu[item.x];
-        const int64_t keys = (int64_t)ctx[item.x] + min((item.y + 1) * span, q);
+        const int64_t keys = (int64_t)ctx[item.x] + prefill_item_end(item.y, q, span / PREFILL_QW);
         const int64_t tiles = (keys + PREFILL_TK - 1) / PREFILL_TK;
         return COST_BUCKETS - 1 - (int)min(tiles, (int64_t)COST_BUCKETS - 1);
     };

@@ -44,6 +44,34 @@ constexpr int decode_part(int head_dim) {
 constexpr int PREFILL_QW = 32;
 constexpr int PREFILL_TK = 64;  // keys per LDS tile
 
+// Position blocks of a prefill work item.  A sequence's q new rows form
+// nb = ceil(q / QW) blocks of QW positions; an item takes npb of them (one
+// per group of HPW waves), and the sequence's T = ceil(nb / npb) items deal
+// them out in snake order: slot k of item t holds block k T + t for even k
+// and k T + T - 1 - t for odd k.  Under the causal mask a block's key count
+// grows with its index, so item 0 of a 2048-row chunk takes blocks 0 and 63
+// rather than 0 and 1, and every item walks about the same number of key
+// tiles with both of its wave groups busy for about the same share of them.
+// A block index >= nb is an empty slot.
+__host__ __device__ inline int prefill_block(int tile, int slot, int per_slot) {
+    return slot * per_slot + ((slot & 1) ? per_slot - 1 - tile : tile);
+}
+// One past the last position that item `tile` of a sequence with q new rows
+// covers (its causal key range ends that many keys past the cached ones).
+__host__ __device__ inline int prefill_item_end(int tile, int q, int npb) {
+    const int nb = (q + PREFILL_QW - 1) / PREFILL_QW;
+    const int T = (nb + npb - 1) / npb;
+    int end = 0;
+    for (int k = 0; k < npb; ++k) {
+        const int b = prefill_block(tile, k, T);
+        if (b < nb) {
+            const int e = (b + 1) * PREFILL_QW < q ? (b + 1) * PREFILL_QW : q;
+            end = e > end ? e : end;
+        }
+    }
+    return end;
+}
+
 struct WsLayout {
     size_t hdr, dec_items, pre_items, pre_sorted, merge_list, ml, acc, total;
     int64_t cap_dec, cap_pre;

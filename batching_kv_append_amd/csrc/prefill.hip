@@ -22,7 +22,9 @@
 // accumulator rescale is rare.
 //
 // Work: one workgroup = NW waves = HPW query heads of one kv group x (NW/HPW)
-// blocks of QW = 32 positions; each wave owns one (head, 32 positions).  A
+// blocks of QW = 32 positions; each wave owns one (head, 32 positions).  The
+// blocks of a sequence are dealt to its workgroups in snake order (an early
+// block with a late one), so their causal key ranges even out.  A
 // call with decode rows takes NW = 4: two workgroups per compute unit, which
 // leaves the co-running decode more of each unit.  A call of chunks only
 // takes NW = 8 up to head_dim 128: one workgroup per compute unit, two waves
@@ -182,8 +184,9 @@ __global__ __launch_bounds__(64 * NW, A > 128 ? 1 : 2) void prefill_kernel(Prefi
     const int qlen = P.cu[s + 1] - row0;
     const int c = P.ctx[s];
     const int L = c + qlen;
-    const int p0 = tile * SPAN + (wave / HPW) * QW;         // first position of this wave
-    const int wg_last = min(tile * SPAN + SPAN, qlen) - 1;  // last position of the workgroup
+    constexpr int NPB = NW / HPW;  // position blocks per workgroup (snake order across items)
+    const int p0 = prefill_block(tile, wave / HPW, (qlen + SPAN - 1) / SPAN) * QW;  // first position of this wave
+    const int wg_last = prefill_item_end(tile, qlen, NPB) - 1;  // last position of the workgroup
     const int nkt = (c + wg_last + 1 + TK - 1) / TK;        // key tiles the workgroup needs
     const int kend_w = (p0 < qlen) ? c + min(p0 + QW, qlen) : 0;  // keys this wave needs
     const float cs = P.scale_log2;

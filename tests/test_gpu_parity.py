@@ -116,6 +116,17 @@ def test_scale_variants(kvc, orc):
     _case(kvc, orc, "scale_big", [(20, 1), (0, 40), (300, 1)], 4, 2, 128, 16, scale=0.5)
 
 
+# A scale <= 0 takes the kernels' other softmax order (scores scaled before the
+# maximum); every decode and prefill instance, mixed and chunks-only calls.
+@pytest.mark.parametrize("a", [16, 64, 128, 256])
+@pytest.mark.parametrize("scale", [0.0, -0.09])
+def test_nonpositive_scale(kvc, orc, a, scale):
+    mixed = [(20, 1), (0, 40), (300, 1), (1100, 1), (70, 100)]
+    _case(kvc, orc, f"scale{scale}_a{a}_mixed", mixed, 8, 2, a, 16, scale=scale)
+    _case(kvc, orc, f"scale{scale}_a{a}_chunks", [(0, 70), (130, 70), (700, 70)], 8, 2, a, 4,
+          scale=scale)
+
+
 def test_toy_chunked_then_decode(kvc, orc):
     """Chunks of 4 and 3 tokens (block size 4), then 8 decode calls; every call
     against the oracle and the chunked rows against the unchunked prefill."""

@@ -127,6 +127,45 @@ def test_nonpositive_scale(kvc, orc, a, scale):
           scale=scale)
 
 
+def _rising_keys(wl, top, seed=5):
+    """Every K row of every sequence becomes s_p * w: one fixed unit direction w
+    per kv head and a magnitude s_p rising linearly with the position p up to
+    `top` at the longest sequence's end.  A query's scores then rise (or fall)
+    steadily along its keys, so the running maximum moves many times inside
+    each tile, partition and work item and the split-K partials carry very
+    different maxima."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    st = wl.steps[0]
+    hkv, a, bs = wl.num_kv_heads, wl.head_dim, wl.block_size
+    w = rng.standard_normal((hkv, a))
+    w /= np.linalg.norm(w, axis=1, keepdims=True)
+    cu, ctx = st.cu_seqlens_q, st.context_lens
+    lmax = int((ctx + np.diff(cu)).max())
+    kp, kn = wl.k_pool.copy(), st.k_new.copy()
+    for s_ in range(st.num_seqs):
+        c, n = int(ctx[s_]), int(cu[s_ + 1] - cu[s_])
+        pos = np.arange(c + n)
+        rows = W.bf16_bits((top * (pos + 1) / lmax)[:, None, None] * w[None].astype(np.float32))
+        kp[st.block_table[s_, pos[:c] // bs], :, pos[:c] % bs, :] = rows[:c]
+        kn[cu[s_]:cu[s_] + n] = rows[c:]
+    return dataclasses.replace(wl, k_pool=kp, steps=[dataclasses.replace(st, k_new=kn)])
+
+
+@pytest.mark.parametrize("a", [16, 64, 128, 256])
+def test_rising_scores(kvc, orc, a):
+    """Scores that climb by about 100 (log2 units) along each sequence: the
+    lazy rescale fires again and again in every kernel, and the merge combines
+    partials whose maxima differ by far more than the rescale slack."""
+    specs = [(5000, 1), (1500, 1), (300, 1), (0, 90), (600, 150), (4100, 1)]
+    wl = W.make_step_workload(f"rising_a{a}", specs, num_q_heads=8, num_kv_heads=2,
+                              head_dim=a, block_size=16, seed=9)
+    wl = _rising_keys(wl, top=800.0 * math.sqrt(a / 128))
+    (g,), _, _ = run_steps(kvc, wl)
+    (r,), _, _ = oracle_run(orc, wl)
+    compare(g, r, what=wl.name)
+
+
 def test_toy_chunked_then_decode(kvc, orc):
     """Chunks of 4 and 3 tokens (block size 4), then 8 decode calls; every call
     against the oracle and the chunked rows against the unchunked prefill."""

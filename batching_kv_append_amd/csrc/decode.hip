@@ -17,13 +17,13 @@
 //     cover whole 128-byte lines;
 //   * the GW query heads that share a kv head (GQA, e2hang/Notes "MQA与GQA")
 //     are served from one read of K/V;
-//   * head_dim 128 (decode_mfma_kernel): a sequence is cut into
+//   * head_dims 64 and 128 (decode_mfma_kernel): a sequence is cut into
 //     ceil(L / 4096) work items of equal length, and a workgroup takes one
 //     item of one (sequence, kv head, head chunk), a quarter of it per wave
 //     (at most one 1024-token partition), scores and P.V on bf16 MFMA; the
 //     four states are combined in LDS, so split-K partials (and the merge)
 //     exist per item;
-//   * head_dim 16, 64 and 256 (decode_kernel): one wave per 256-token
+//   * head_dims 16 and 256 (decode_kernel): one wave per 256-token
 //     partition, dot products reduced across the lanes of a token row.
 // The planning kernel lists the work items on the device, longest pieces
 // first, so the host needs no copy of the lengths, and the hardware
@@ -495,13 +495,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode partial kernel on the matrix cores (head_dim 128).
+// Decode partial kernel on the matrix cores (head_dims 64 and 128).
 //
 // Both products of a decode step are small matrix products once the query
 // heads that share a kv head are stacked as columns (up to 16):
 //   S^T[token][head] = K[token][:] . Q^T[:][head]      v_mfma_f32_16x16x32_bf16
 //   O^T[dim][head]  += V^T[dim][token] . P^T[token][head]
-// K rows are loaded whole and rearranged through a per-wave 8 KiB LDS tile
+// K rows are loaded whole and rearranged through a per-wave LDS tile (A x 64 B)
 // into the A operand (lane l owns token l%16 of a 16-token block and 8 dims
 // of each 32-dim step); the score registers of a lane (head l%16, tokens
 // 4g..4g+3 of each block, g = l/16) are already the B operand of the second
@@ -539,11 +539,17 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // are still read (a padded batch streams every position), their scores are
 // excluded by select and their V rows are zeroed, so whatever the padding
 // holds has weight exactly 0.
-template <int BS, int NG, bool MASKED>
+template <int A, int BS, int NG, bool MASKED>
 __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(DecodeParams P) {
-    constexpr int A = 128;
+    static_assert(A == 64 || A == 128, "matrix decode: head_dim 64 or 128");
     constexpr int CPR = A / 8;              // 16-byte chunks per row
     constexpr int STEP = 32;                // tokens per matrix step
+    constexpr int RPL = 64 / CPR;           // whole K rows per load instruction (4 or 8)
+    constexpr int NKL = STEP / RPL;         // K load instructions per step
+    constexpr int KS = A / 32;              // 32-dim steps of S^T = K Q^T
+    constexpr int DT = A / 16;              // 16-dim tiles of O^T
+    constexpr int VPL = 64 / CPR;           // 4-token V row groups per load instruction
+    constexpr int NVG = 8 / VPL;            // 4-token V row groups per lane (2, or 1 at head_dim 64)
     constexpr int DP = DECODE_PART_MFMA;    // partition length: at most one wave's tokens
     constexpr int NT = DP / BS;             // table entries per wave, at most
     constexpr int NTV = (NT + 63) / 64;     // VGPRs holding them (4 for 4-token blocks)
@@ -564,6 +570,8 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     const int lane = threadIdx.x & 63;
     const int col = lane & 15;  // head column
     const int g = lane >> 4;    // token group: tokens 4g..4g+3 of each 16-token block
+    const int lr = lane / CPR;  // loads: row (K) or 4-row group (V) of this lane in one instruction
+    const int lc = lane % CPR;  // loads: 16-byte chunk of this lane (dims 8 lc .. 8 lc + 7)
     const int64_t n_units = (int64_t)P.hdr[HDR_N_DEC] * P.hkv * P.HC;
     const int64_t u = blockIdx.x;
     if (u >= n_units) return;  // the whole workgroup
@@ -615,22 +623,22 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
 
     // Q^T operand of group ng: column col = head h0 + 16ng + col (zero past
     // GW), dims 32ks + 8g .. +7
-    uint4 qb[NG][4];
+    uint4 qb[NG][KS];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             qb[ng][ks] = make_uint4(0, 0, 0, 0);
             if (16 * ng + col < GW)
                 qb[ng][ks] = *reinterpret_cast<const uint4*>(
                     P.q + (((int64_t)row * P.hq + h0 + 16 * ng + col) * A + ks * 32 + g * 8));
         }
 
-    f32x4_t o[NG][8];  // O^T rows 16dt + 4g + r, column col of group ng
+    f32x4_t o[NG][DT];  // O^T rows 16dt + 4g + r, column col of group ng
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[ng][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < DT; ++dt) o[ng][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m[NG], lsum[NG];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
@@ -670,43 +678,60 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     // The table register that holds the entries of the step at tc (a uniform
     // choice).  A step at or past t1 reads only token t1 - 1 (every token is
     // clamped to it), so it takes that token's register.
+    static_assert(NTV == 1 || NTV == 4, "table slice registers");
     auto table_reg = [&](int tc) -> int {
-        int tv = tbl[0];
-        const int sel = ((min(tc, t1 - 1) - t0) / BS) >> 6;
-#pragma unroll
-        for (int v = 1; v < NTV; ++v)
-            if (sel == v) tv = tbl[v];
-        return tv;
+        if constexpr (NTV == 1) {
+            return tbl[0];
+        } else {
+            // a branch per register (a select chain can be turned into an
+            // indexed stack array)
+            switch (((min(tc, t1 - 1) - t0) / BS) >> 6) {
+                case 0: return tbl[0];
+                case 1: return tbl[1];
+                case 2: return tbl[2];
+                default: return tbl[3];
+            }
+        }
     };
-    // ---- K: 32 rows, four per load, each row whole (16 lanes x 16 B) --
-    // Lane (g, col) of load j reads chunk col of row 4j + g; the rows then
-    // pass through the wave's LDS tile into the MFMA operand layout.
-    uint4 kst[8];
+    // ---- K: 32 rows, RPL per load, each row whole (CPR lanes x 16 B) --
+    // Lane (lr, lc) of load j reads chunk lc of row RPL j + lr; the rows then
+    // pass through the wave's LDS tile into the MFMA operand layout.  The
+    // rows of one load share a 16-token block.
+    uint4 kst[NKL];
     auto load_k = [&](int tc) __attribute__((always_inline)) {
         const int tv = table_reg(tc);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = min(tc + 4 * j + g, t1 - 1);
-            int64_t blk = block_of(tv, t, min(tc + 16 * (j >> 2), t1 - 1));
+        for (int j = 0; j < NKL; ++j) {
+            const int t = min(tc + RPL * j + lr, t1 - 1);
+            int64_t blk = block_of(tv, t, min(tc + 16 * (RPL * j / 16), t1 - 1));
             if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
-            kst[j] = v_stream(P.k_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col);
+            kst[j] = v_stream(P.k_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + lc);
         }
     };
-    // ---- V: token groups g and g+4 (4 tokens each) x chunk col --------
-    // Each load instruction reads four whole 256-byte rows; rows past the
-    // end repeat the last row (their weight is 0).  No branch: the two sides
-    // of one would load into the same registers, and the second side would
-    // wait for every load in flight.
-    uint4 vb[2][4];
+    // ---- V: 4-token groups lr + VPL h (h < NVG) x chunk lc ---------------
+    // Each load instruction reads VPL whole rows; rows past the end repeat
+    // the last row (their weight is 0).  No branch: the two sides of one
+    // would load into the same registers, and the second side would wait for
+    // every load in flight.  At head_dim 64 the 8 groups of one instruction
+    // span both 16-token halves of the step, so with 16-token blocks the lane
+    // picks one of the two halves' entries.
+    uint4 vb[NVG][4];
     auto load_v = [&](int tc) __attribute__((always_inline)) {
         const int tv = table_reg(tc);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int tg = g + 4 * hh;
+        for (int hh = 0; hh < NVG; ++hh) {
+            const int tg = lr + VPL * hh;
             const int t = min(tc + 4 * tg, t1 - 1);
-            int64_t blk = block_of(tv, t, min(tc + 16 * hh, t1 - 1));
+            int64_t blk;
+            if constexpr (BS == 16 && VPL > 4) {
+                const int64_t b0 = block_of(tv, t, min(tc, t1 - 1));
+                const int64_t b1 = block_of(tv, t, min(tc + 16, t1 - 1));
+                blk = tg >= 4 ? b1 : b0;
+            } else {
+                blk = block_of(tv, t, min(tc + 16 * (VPL * hh / 4), t1 - 1));
+            }
             if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
-            const uint4* vp = P.v_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + col;
+            const uint4* vp = P.v_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + lc;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 vb[hh][j] = v_stream(vp + (min(tc + 4 * tg + j, t1 - 1) - t) * CPR);
@@ -738,28 +763,28 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         const bool padded = MASKED && tc < kstart;  // some key of this step is padding
         if (padded) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+            for (int hh = 0; hh < NVG; ++hh)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (tc + 4 * (g + 4 * hh) + j < kstart) vb[hh][j] = make_uint4(0, 0, 0, 0);
+                    if (tc + 4 * (lr + VPL * hh) + j < kstart) vb[hh][j] = make_uint4(0, 0, 0, 0);
         }
 
-        // K rows into this wave's tile ([row][chunk ^ row % 16]), then the
+        // K rows into this wave's tile ([row][chunk ^ row % CPR]), then the
         // A operands: lane (g, col) of block b, step ks takes chunk 4 ks + g
         // of row 16 b + col.  The V^T stores below reuse the tile after these
         // reads (same wave, in order).
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = 4 * j + g;
-            vt[r * 16 + (col ^ (r & 15))] = kst[j];
+        for (int j = 0; j < NKL; ++j) {
+            const int r = RPL * j + lr;
+            vt[r * CPR + (lc ^ (r % CPR))] = kst[j];
         }
-        uint4 kb[2][4];
+        uint4 kb[2][KS];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 const int r = 16 * b + col;
-                kb[b][ks] = vt[r * 16 + ((4 * ks + g) ^ (r & 15))];
+                kb[b][ks] = vt[r * CPR + ((4 * ks + g) ^ (r % CPR))];
             }
         if (PF) load_k(tc_next);
 
@@ -771,7 +796,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             for (int b = 0; b < 2; ++b) {
                 sc[ng][b] = mfma16(kb[b][0], qb[ng][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int ks = 1; ks < 4; ++ks) sc[ng][b] = mfma16(kb[b][ks], qb[ng][ks], sc[ng][b]);
+                for (int ks = 1; ks < KS; ++ks) sc[ng][b] = mfma16(kb[b][ks], qb[ng][ks], sc[ng][b]);
             }
 
         // ---- V^T into LDS (this wave's tile): 8-byte units of 4 tokens ------
@@ -779,7 +804,8 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         // (element-wise extracts would let the optimizer split each 16-byte
         // row load into four 4-byte loads).
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < NVG; ++hh) {
+            const int tg = lr + VPL * hh;  // tokens 4 tg .. 4 tg + 3 of the step
             const u16x8_t r0 = __builtin_bit_cast(u16x8_t, vb[hh][0]);
             const u16x8_t r1 = __builtin_bit_cast(u16x8_t, vb[hh][1]);
             const u16x8_t r2 = __builtin_bit_cast(u16x8_t, vb[hh][2]);
@@ -790,11 +816,14 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             const u32x8_t t23 = __builtin_bit_cast(u32x8_t, __builtin_shufflevector(
                 r2, r3, 0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15));
             uint2* vt2 = reinterpret_cast<uint2*>(vt);
+            // row d, 16-byte chunk tg % 4 (tokens 4(tg%4).. and 16+4(tg%4)..),
+            // half tg / 4 (with 4 groups per instruction: lr and hh)
+            const int gq = VPL == 4 ? lr : (tg & 3);
+            const int half = VPL == 4 ? hh : (tg >> 2);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int d = col * 8 + e;
-                // row d, 16-byte chunk g (tokens 4g.. and 16+4g..), half hh
-                vt2[(d * 4 + (g ^ ((d >> 2) & 3))) * 2 + hh] = make_uint2(t01[e], t23[e]);
+                const int d = lc * 8 + e;
+                vt2[(d * 4 + (gq ^ ((d >> 2) & 3))) * 2 + half] = make_uint2(t01[e], t23[e]);
             }
         }
         if (PF) load_v(tc_next);
@@ -834,7 +863,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
                 m[ng] = m_new;
                 lsum[ng] *= alpha;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[ng][dt] *= alpha;
+                for (int dt = 0; dt < DT; ++dt) o[ng][dt] *= alpha;
             }
             float p[8];
 #pragma unroll
@@ -852,7 +881,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
 
         // ---- O^T += V^T P^T (one V^T fragment for all head groups) ------------
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
+        for (int dt = 0; dt < DT; ++dt) {
             const int d = dt * 16 + col;
             const uint4 a = vt[d * 4 + (g ^ ((d >> 2) & 3))];
 #pragma unroll
@@ -874,10 +903,10 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         lt[ng] += __shfl_xor(lt[ng], 32, 64);
     }
     // normalised bf16 output of column group ng (scaled by inv)
-    auto write_out = [&](int ng, const f32x4_t (&acc)[8], float inv) {
+    auto write_out = [&](int ng, const f32x4_t (&acc)[DT], float inv) {
         uint16_t* orow = P.out + ((int64_t)row * P.hq + h0 + 16 * ng + col) * A;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
+        for (int dt = 0; dt < DT; ++dt) {
             uint2 v;
             v.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
             v.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
@@ -885,11 +914,11 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         }
     };
     // split-K partial (max, total, fp32 accumulator) of work item `item`
-    auto write_partial = [&](int ng, const f32x4_t (&acc)[8], float mm, float ll) {
+    auto write_partial = [&](int ng, const f32x4_t (&acc)[DT], float mm, float ll) {
         const int64_t slot = (int64_t)item * P.hq + h0 + 16 * ng + col;
         float* dst = P.ws_acc + slot * A;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
             *reinterpret_cast<float4*>(dst + dt * 16 + 4 * g) =
                 make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
         if (g == 0) {
@@ -917,8 +946,8 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
                 sML[wave][1][16 * ng + col] = lt[ng];
             }
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                mine[(ng * 8 + dt) * 64 + lane] =
+            for (int dt = 0; dt < DT; ++dt)
+                mine[(ng * DT + dt) * 64 + lane] =
                     make_float4(o[ng][dt][0], o[ng][dt][1], o[ng][dt][2], o[ng][dt][3]);
         }
         __threadfence_block();  // this wave's LDS writes before its arrival
@@ -933,16 +962,16 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
             float mm = -INFINITY;
             for (int w = 0; w < nact; ++w) mm = fmaxf(mm, sML[w][0][c16]);
             float ll = 0.f;
-            f32x4_t acc[8];
+            f32x4_t acc[DT];
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             for (int w = 0; w < nact; ++w) {
                 const float sc = __builtin_amdgcn_exp2f(sML[w][0][c16] - mm);
                 ll += sc * sML[w][1][c16];
                 const float4* src = reinterpret_cast<const float4*>(&sVt[w][0]);
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) {
-                    const float4 v = src[(ng * 8 + dt) * 64 + lane];
+                for (int dt = 0; dt < DT; ++dt) {
+                    const float4 v = src[(ng * DT + dt) * 64 + lane];
                     acc[dt][0] += sc * v.x;
                     acc[dt][1] += sc * v.y;
                     acc[dt][2] += sc * v.z;
@@ -960,7 +989,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
 // ---------------------------------------------------------------------------
 // Merge kernel: one wave per (decode sequence with several work items, query
 // head); a work item's partial covers one partition group (one partition on
-// the vector-ALU path of head_dims 16, 64 and 256).
+// the vector-ALU path of head_dims 16 and 256).
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // The plan's descriptor carries everything the wave needs, and the (m, l)
 // pairs and accumulators of up to 32 partials are requested together, so a
@@ -1056,10 +1085,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
     }
 }
 
-template <int BS, bool MASKED>
+template <int A, int BS, bool MASKED>
 void launch_decode_mfma(const StepArgs& a, const DecodeParams& p, bool two, int grid) {
-    if (two) hipLaunchKernelGGL((decode_mfma_kernel<BS, 2, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<BS, 1, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
+    if (two) hipLaunchKernelGGL((decode_mfma_kernel<A, BS, 2, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<A, BS, 1, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
 }
 
 template <int A, int BS, int GW>
@@ -1080,7 +1109,7 @@ void launch_decode_gw(const StepArgs& a, const DecodeParams& p, int GW, int grid
 }  // namespace
 
 int decode_heads_per_wave(int G, int head_dim) {
-    if (head_dim == 128) {  // matrix path: 32 when G is a multiple of 32 (two column
+    if (decode_on_mfma(head_dim)) {  // matrix path: 32 when G is a multiple of 32 (two column
         if (G % 32 == 0) return 32;  // groups), else the largest divisor of G <= 16
         for (int gw = G < 16 ? G : 16; gw > 1; --gw)
             if (G % gw == 0) return gw;
@@ -1157,15 +1186,19 @@ hipError_t launch_decode(const StepArgs& a) {
     if (grid64 <= 0) return hipSuccess;
     if (grid64 > INT32_MAX) return hipErrorInvalidValue;
     const int grid = (int)grid64;
-    if (a.head_dim == 128) {
+    if (decode_on_mfma(a.head_dim)) {
         const bool two = GW > 16;  // 32 heads per wave: two MFMA column groups
         if (gp != 4) return hipErrorInvalidValue;  // the matrix decode works in partition groups
-        if (a.key_start) {
-            if (a.block_size == 16) launch_decode_mfma<16, true>(a, p, two, grid);
-            else launch_decode_mfma<4, true>(a, p, two, grid);
+        if (a.key_start) {  // the left-padded batch (head_dim 128 only)
+            if (a.head_dim != 128) return hipErrorInvalidValue;
+            if (a.block_size == 16) launch_decode_mfma<128, 16, true>(a, p, two, grid);
+            else launch_decode_mfma<128, 4, true>(a, p, two, grid);
+        } else if (a.head_dim == 128) {
+            if (a.block_size == 16) launch_decode_mfma<128, 16, false>(a, p, two, grid);
+            else launch_decode_mfma<128, 4, false>(a, p, two, grid);
         } else {
-            if (a.block_size == 16) launch_decode_mfma<16, false>(a, p, two, grid);
-            else launch_decode_mfma<4, false>(a, p, two, grid);
+            if (a.block_size == 16) launch_decode_mfma<64, 16, false>(a, p, two, grid);
+            else launch_decode_mfma<64, 4, false>(a, p, two, grid);
         }
     } else {
         // the other head sizes take the vector-ALU decode (one partition per wave)
@@ -1173,10 +1206,6 @@ hipError_t launch_decode(const StepArgs& a) {
             case 16:
                 if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);
                 else launch_decode_gw<16, 4>(a, p, GW, grid);
-                break;
-            case 64:
-                if (a.block_size == 16) launch_decode_gw<64, 16>(a, p, GW, grid);
-                else launch_decode_gw<64, 4>(a, p, GW, grid);
                 break;
             default:
                 if (a.block_size == 16) launch_decode_gw<256, 16>(a, p, GW, grid);

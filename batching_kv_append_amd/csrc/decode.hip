@@ -17,13 +17,13 @@
 //     cover whole 128-byte lines;
 //   * the GW query heads that share a kv head (GQA, e2hang/Notes "MQA与GQA")
 //     are served from one read of K/V;
-//   * head_dims 64 and 128 (decode_mfma_kernel): a sequence is cut into
+//   * head_dims 64, 128 and 256 (decode_mfma_kernel): a sequence is cut into
 //     ceil(L / 4096) work items of equal length, and a workgroup takes one
 //     item of one (sequence, kv head, head chunk), a quarter of it per wave
 //     (at most one 1024-token partition), scores and P.V on bf16 MFMA; the
 //     four states are combined in LDS, so split-K partials (and the merge)
 //     exist per item;
-//   * head_dims 16 and 256 (decode_kernel): one wave per 256-token
+//   * head_dim 16 (decode_kernel): one wave per 256-token
 //     partition, dot products reduced across the lanes of a token row.
 // The planning kernel lists the work items on the device, longest pieces
 // first, so the host needs no copy of the lengths, and the hardware
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode partial kernel on the matrix cores (head_dims 64 and 128).
+// Decode partial kernel on the matrix cores (head_dims 64, 128 and 256).
 //
 // Both products of a decode step are small matrix products once the query
 // heads that share a kv head are stacked as columns (up to 16):
@@ -534,14 +534,18 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // output (a sequence of one item) or into one split-K partial per item.
 // The two-group kernel is held to two waves per SIMD (at most 256 VGPRs; it
 // fits in 228 without spills): left free it takes about 300 and runs one wave
-// per SIMD, too few loads in flight for a memory-bound kernel.
+// per SIMD, too few loads in flight for a memory-bound kernel.  Head_dim 256
+// takes one group only (two would spill): its accumulators and operands fill
+// about 350 registers, one wave per SIMD, and 32 heads on one kv head run as
+// two head chunks whose workgroups share an XCD (the second reads K/V from
+// its L2).
 // MASKED (the left-padded batch): keys below key_start[s] are padding.  They
 // are still read (a padded batch streams every position), their scores are
 // excluded by select and their V rows are zeroed, so whatever the padding
 // holds has weight exactly 0.
 template <int A, int BS, int NG, bool MASKED>
 __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(DecodeParams P) {
-    static_assert(A == 64 || A == 128, "matrix decode: head_dim 64 or 128");
+    static_assert(A == 64 || A == 128 || A == 256, "matrix decode: head_dim 64, 128 or 256");
     constexpr int CPR = A / 8;              // 16-byte chunks per row
     constexpr int STEP = 32;                // tokens per matrix step
     constexpr int RPL = 64 / CPR;           // whole K rows per load instruction (4 or 8)
@@ -572,17 +576,24 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     const int g = lane >> 4;    // token group: tokens 4g..4g+3 of each 16-token block
     const int lr = lane / CPR;  // loads: row (K) or 4-row group (V) of this lane in one instruction
     const int lc = lane % CPR;  // loads: 16-byte chunk of this lane (dims 8 lc .. 8 lc + 7)
-    const int64_t n_units = (int64_t)P.hdr[HDR_N_DEC] * P.hkv * P.HC;
-    const int64_t u = blockIdx.x;
-    if (u >= n_units) return;  // the whole workgroup
+    // Workgroup -> (work item, kv head, head chunk).  Workgroups go to the 8
+    // XCDs round-robin by linear id, each XCD with its own L2; the head
+    // chunks of one (item, kv head) are 8 ids apart, so they run on one XCD
+    // at about the same time and all but the first find the K/V rows in its
+    // L2.  The grid covers the capacity (rounded up to 8 pairs for chunks);
+    // workgroups past the planned count leave at once.
+    const int64_t n_pairs = (int64_t)P.hdr[HDR_N_DEC] * P.hkv;
+    const int64_t lid = blockIdx.x;
+    const int64_t pair = P.HC == 1 ? lid : (lid >> 3) / P.HC * 8 + (lid & 7);
+    if (pair >= n_pairs) return;  // the whole workgroup
     if (threadIdx.x == 0) arrived = 0;
     __syncthreads();  // the only barrier: waves past the sequence leave below
     uint4* vt = &sVt[wave][0];
 
     const int GW = P.G / P.HC;  // heads of this wave (<= 16 * NG)
-    const int hc = u % P.HC;
-    const int kvh = (u / P.HC) % P.hkv;
-    const int item = u / (P.HC * P.hkv);
+    const int hc = P.HC == 1 ? 0 : (int)((lid >> 3) % P.HC);
+    const int kvh = pair % P.hkv;
+    const int item = pair / P.hkv;
     const int2 it = P.items[item];
     const int s = it.x;
     const int L = P.ctx[s] + 1;
@@ -989,7 +1000,7 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
 // ---------------------------------------------------------------------------
 // Merge kernel: one wave per (decode sequence with several work items, query
 // head); a work item's partial covers one partition group (one partition on
-// the vector-ALU path of head_dims 16 and 256).
+// the vector-ALU path of head_dim 16).
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // The plan's descriptor carries everything the wave needs, and the (m, l)
 // pairs and accumulators of up to 32 partials are requested together, so a
@@ -1087,8 +1098,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
 
 template <int A, int BS, bool MASKED>
 void launch_decode_mfma(const StepArgs& a, const DecodeParams& p, bool two, int grid) {
-    if (two) hipLaunchKernelGGL((decode_mfma_kernel<A, BS, 2, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<A, BS, 1, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
+    if constexpr (A <= 128) {  // head_dim 256: one column group (registers)
+        if (two) {
+            hipLaunchKernelGGL((decode_mfma_kernel<A, BS, 2, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((decode_mfma_kernel<A, BS, 1, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
 }
 
 template <int A, int BS, int GW>
@@ -1110,7 +1126,7 @@ void launch_decode_gw(const StepArgs& a, const DecodeParams& p, int GW, int grid
 
 int decode_heads_per_wave(int G, int head_dim) {
     if (decode_on_mfma(head_dim)) {  // matrix path: 32 when G is a multiple of 32 (two column
-        if (G % 32 == 0) return 32;  // groups), else the largest divisor of G <= 16
+        if (G % 32 == 0 && head_dim <= 128) return 32;  // groups), else the largest divisor of G <= 16
         for (int gw = G < 16 ? G : 16; gw > 1; --gw)
             if (G % gw == 0) return gw;
         return 1;
@@ -1178,11 +1194,13 @@ hipError_t launch_decode(const StepArgs& a) {
     p.G = G;
     p.HC = G / GW;
     p.scale_log2 = a.scale * 1.4426950408889634f;
-    // Matrix decode: one workgroup per unit (a group of four partitions)
-    // over the upper bound of units; head_dim 16: one wave per unit.
     const int gp = decode_group_parts(G, a.head_dim);
     const int64_t units = a.lay.cap_dec * a.num_kv_heads * p.HC;
-    const int64_t grid64 = gp > 1 ? units : (units + 3) / 4;
+    // matrix decode: one workgroup per unit, the head chunks of one (item, kv
+    // head) 8 launch ids apart (so the pairs are padded to a multiple of 8);
+    // vector-ALU decode: one wave per unit
+    const int64_t pairs8 = (a.lay.cap_dec * a.num_kv_heads + 7) / 8 * 8;
+    const int64_t grid64 = gp > 1 ? (p.HC == 1 ? units : pairs8 * p.HC) : (units + 3) / 4;
     if (grid64 <= 0) return hipSuccess;
     if (grid64 > INT32_MAX) return hipErrorInvalidValue;
     const int grid = (int)grid64;
@@ -1196,22 +1214,18 @@ hipError_t launch_decode(const StepArgs& a) {
         } else if (a.head_dim == 128) {
             if (a.block_size == 16) launch_decode_mfma<128, 16, false>(a, p, two, grid);
             else launch_decode_mfma<128, 4, false>(a, p, two, grid);
-        } else {
+        } else if (a.head_dim == 64) {
             if (a.block_size == 16) launch_decode_mfma<64, 16, false>(a, p, two, grid);
             else launch_decode_mfma<64, 4, false>(a, p, two, grid);
+        } else {
+            if (a.block_size == 16) launch_decode_mfma<256, 16, false>(a, p, two, grid);
+            else launch_decode_mfma<256, 4, false>(a, p, two, grid);
         }
     } else {
-        // the other head sizes take the vector-ALU decode (one partition per wave)
-        switch (a.head_dim) {
-            case 16:
-                if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);
-                else launch_decode_gw<16, 4>(a, p, GW, grid);
-                break;
-            default:
-                if (a.block_size == 16) launch_decode_gw<256, 16>(a, p, GW, grid);
-                else launch_decode_gw<256, 4>(a, p, GW, grid);
-                break;
-        }
+        // head_dim 16 takes the vector-ALU decode (one partition per wave)
+        if (a.head_dim != 16) return hipErrorInvalidValue;
+        if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);
+        else launch_decode_gw<16, 4>(a, p, GW, grid);
     }
     return hipGetLastError();
 }

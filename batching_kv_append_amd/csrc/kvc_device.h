@@ -27,7 +27,7 @@ enum Flag : int {
 // Decode partition length in tokens: at most what one wave walks.  Fixed per
 // head size (never chosen per batch), so a sequence's partial sums depend only
 // on its own logical positions and the output does not change with batch
-// composition.  The matrix decode (head_dims 64 and 128) takes 1024: fewer, longer
+// composition.  The matrix decode (head_dims 64, 128, 256) takes 1024: fewer, longer
 // waves write fewer split-K partials and pay their start-up (table slice, Q
 // operand, first loads) and their combine less often (GQA batch 237 -> 226 us,
 // MQA 141 -> 130 us, mixed step 0.81 -> 0.77 ms against 256).  The vector-ALU
@@ -35,7 +35,7 @@ enum Flag : int {
 constexpr int DECODE_PART_MFMA = 1024;
 constexpr int DECODE_PART_VALU = 256;
 // Head sizes the matrix decode serves (the others take the vector-ALU one).
-constexpr bool decode_on_mfma(int head_dim) { return head_dim == 64 || head_dim == 128; }
+constexpr bool decode_on_mfma(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
 constexpr int decode_part(int head_dim) {
     return decode_on_mfma(head_dim) ? DECODE_PART_MFMA : DECODE_PART_VALU;
 }
@@ -85,11 +85,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int prefill_hpw(int G) { return G >= 4 ? 4 : G; }
 inline int prefill_span(int G, int nw = 4) { return PREFILL_QW * (nw / prefill_hpw(G)); }
 
-// Decode partitions per work item: the matrix decode (head_dims 64, 128) cuts a
+// Decode partitions per work item: the matrix decode (head_dims 64-256) cuts a
 // sequence into ceil(L / (4 * DECODE_PART_MFMA)) equal items, gives each of a
 // workgroup's four waves a quarter of one item and combines them in LDS, so
-// split-K partials exist per item; the vector-ALU decode (head_dims 16 and
-// 256) takes one partition per wave.
+// split-K partials exist per item; the vector-ALU decode (head_dim 16) takes
+// one partition per wave.
 constexpr int DECODE_GROUP = 4;  // partitions per matrix-decode workgroup (its four waves)
 inline int decode_group_parts(int G, int head_dim) {
     (void)G;

@@ -62,7 +62,7 @@ def _chunks_only_case(i):
 
 
 CASES = [_case(i) for i in range(N_CASES)]
-# head dims 64 and 256 (the vector-ALU decode and the prefill instances of those sizes)
+# head dims 64 and 256 (the matrix decode and prefill instances of those sizes)
 CASES += [_case(i, dims=(64, 256)) for i in range(N_CASES, N_CASES + 12)]
 # chunks only (the 8-wave prefill with P.V a tile late on half the waves)
 CASES += [_chunks_only_case(i) for i in range(10)]

@@ -193,7 +193,7 @@ BASELINES_DESC = ("GQA decode batch (256 sequences, 32/8 heads, head_dim 128, co
 
 
 def time_decode_batch(kvc, ctx, hq, hkv, a, bs, steps, warmup, seed=0, reserve_len=None,
-                      padded=False):
+                      padded=False, phases=False):
     """Microseconds per call of one decode batch (one new token per sequence at
     the given contexts) on random GPU-drawn data.  Paged: each sequence holds
     just the blocks it needs, in shuffled pool order.  reserve_len set: a
@@ -202,7 +202,8 @@ def time_decode_batch(kvc, ctx, hq, hkv, a, bs, steps, warmup, seed=0, reserve_l
     padded: the left-padded batch (kvc_padded_decode_attention): every
     sequence holds n_max = the longest one's length, rounded up to whole
     blocks, its tokens right-aligned after pad positions that are read and
-    masked."""
+    masked.  phases: also time each kernel with HIP events in a second pass
+    and return (us, {phase: us per call})."""
     s = len(ctx)
     nblk = [-(-(int(c) + 1) // bs) for c in ctx]
     g = torch.Generator(device="cuda").manual_seed(seed)
@@ -252,10 +253,60 @@ def time_decode_batch(kvc, ctx, hq, hkv, a, bs, steps, warmup, seed=0, reserve_l
         call()
     torch.cuda.synchronize()
     us = (time.perf_counter() - t0) * 1e6 / steps
+    ph = None
+    if phases:
+        kvc.kvc_profile_begin(steps)
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        ms, n = kvc.kvc_profile_end()
+        ph = {k: v * 1e3 / n for k, v in ms.items()}
     if not padded:
         assert kvc.kvc_workspace_flags(ws) == 0
     del kc, vc
-    return us
+    return (us, ph) if phases else us
+
+
+HEADDIMS_DESC = ("decode batches of 256 sequences (one new token each) at head_dim 16, 64, 128 "
+                 "and 256, block 16: GQA 32/8 heads with decode_gqa's contexts and MQA 32/1 "
+                 "with decode_mqa's")
+
+
+def run_headdims(args, kvc):
+    """Decode kernel bandwidth per head size, GQA and MQA (random GPU-drawn
+    data, shuffled paged blocks)."""
+    torch.cuda.set_device(0)
+    table = []
+    for name, hq, hkv, seed, med, lo, hi in [("gqa", 32, 8, 2, 1024.0, 16, 8192),
+                                             ("mqa", 32, 1, 5, 4096.0, 64, 32768)]:
+        rng = np.random.default_rng(seed)
+        ctx = [int(c) for c in np.clip(np.rint(np.exp(rng.normal(math.log(med), 0.8, size=256))),
+                                       lo, hi)]
+        for a in (16, 64, 128, 256):
+            us, ph = time_decode_batch(kvc, ctx, hq, hkv, a, 16, args.steps, args.warmup,
+                                       phases=True)
+            kv_bytes = float(sum(c + 1 for c in ctx)) * hkv * a * 2 * 2
+            gbps = kv_bytes / (ph["decode"] * 1e-6) / 1e9
+            table.append({"heads": f"{hq}/{hkv}", "head_dim": a, "kv_bytes": kv_bytes,
+                          "step_us": us, "decode_us": ph["decode"], "merge_us": ph["merge"],
+                          "decode_gbps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS})
+            print(f"# {name} head_dim {a}: decode {ph['decode']:.1f} us, {gbps:.0f} GB/s "
+                  f"({gbps / HBM_PEAK_GBPS:.2f} of peak)", file=sys.stderr, flush=True)
+    ref = next(r for r in table if r["heads"] == "32/8" and r["head_dim"] == 128)
+    result = {
+        "metric": METRIC, "value": 256 / (ref["step_us"] * 1e-6), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ref["step_us"] / 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded lengths; GPU-drawn random K/V and rows)",
+        "config": {"workload": HEADDIMS_DESC, "name": "headdims"},
+        "roofline": {"bound": "hbm", "kernel": "decode kernels (GQA head_dim 128 batch)",
+                     "achieved": ref["decode_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": ref["frac_hbm_peak"], "traffic": None,
+                     "algorithmic_bytes_per_launch": ref["kv_bytes"],
+                     "avg_launch_us": ref["decode_us"]},
+        "head_dims": table,
+    }
+    print(json.dumps(result), flush=True)
 
 
 def run_baselines(args, kvc):
@@ -584,7 +635,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS) + ["serve", "baselines"],
+    ap.add_argument("--workload", default="mixed",
+                    choices=sorted(WORKLOADS) + ["serve", "baselines", "headdims"],
                     help="serve: scheduler-driven steps over a request trace (use e.g. "
                          "--steps 300 --warmup 300)")
     ap.add_argument("--seed", type=int, default=None)
@@ -619,6 +671,9 @@ def main():
         return
     if args.workload == "baselines":
         run_baselines(args, kvc)
+        return
+    if args.workload == "headdims":
+        run_headdims(args, kvc)
         return
     desc, make = WORKLOADS[args.workload]
     t0 = time.perf_counter()

@@ -56,7 +56,7 @@ struct PrepParams {
     int32_t* hdr;
     int2* dec_items;
     int2* pre_items;
-    int2* pre_sorted;
+    PreItem* pre_sorted;
     int4* merge_list;  // (sequence, first item, items, output row)
     // append (k_new == nullptr: nothing to append)
     const uint4* k_new;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     int32_t* hdr = P.hdr;
     int2* dec_items = P.dec_items;
     int2* pre_items = P.pre_items;
-    int2* pre_sorted = P.pre_sorted;
+    PreItem* pre_sorted = P.pre_sorted;
     int4* merge_list = P.merge_list;
     __shared__ int wsum[3][WAVES];
     __shared__ int hist[COST_BUCKETS];
@@ -264,7 +264,15 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     for (int i = tid; i < npre; i += PLAN_THREADS) {
         const int2 item = pre_items[i];
         const int at = atomicAdd(&hist[bucket_of(item)], 1);
-        pre_sorted[at] = item;
+        const int row0 = cu[item.x];
+        PreItem rec;
+        rec.s = item.x;
+        rec.tile = item.y;
+        rec.row0 = row0;
+        rec.qlen = cu[item.x + 1] - row0;
+        rec.ctx = ctx[item.x];
+        rec.pad0 = rec.pad1 = rec.pad2 = 0;
+        pre_sorted[at] = rec;
     }
     if (tid == 0) {
         const int first = num_seqs > 0 ? cu_ends[0] : cu[0];
@@ -1152,7 +1160,7 @@ hipError_t launch_prep(const StepArgs& a, bool with_append) {
     p.hdr = (int32_t*)(ws + a.lay.hdr);
     p.dec_items = (int2*)(ws + a.lay.dec_items);
     p.pre_items = (int2*)(ws + a.lay.pre_items);
-    p.pre_sorted = (int2*)(ws + a.lay.pre_sorted);
+    p.pre_sorted = (PreItem*)(ws + a.lay.pre_sorted);
     p.merge_list = (int4*)(ws + a.lay.merge_list);
     p.k_new = with_append ? (const uint4*)a.k_new : nullptr;
     p.v_new = with_append ? (const uint4*)a.v_new : nullptr;

@@ -74,6 +74,15 @@ __host__ __device__ inline int prefill_item_end(int tile, int q, int npb) {
     return end;
 }
 
+// A prefill work item as the planner hands it to the prefill kernel: the
+// sequence, the item's index among its T items, and the sequence's first row,
+// new-row count and cached length, so a workgroup reads everything it needs
+// before its table lookups in one memory round trip.
+struct PreItem {
+    int32_t s, tile, row0, qlen;
+    int32_t ctx, pad0, pad1, pad2;
+};
+
 struct WsLayout {
     size_t hdr, dec_items, pre_items, pre_sorted, merge_list, ml, acc, total;
     int64_t cap_dec, cap_pre;
@@ -109,7 +118,7 @@ inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context
     w.hdr = off;        off = align_up(off + HDR_WORDS * 4, 256);
     w.dec_items = off;  off = align_up(off + (size_t)w.cap_dec * 8, 256);
     w.pre_items = off;  off = align_up(off + (size_t)w.cap_pre * 8, 256);
-    w.pre_sorted = off; off = align_up(off + (size_t)w.cap_pre * 8, 256);
+    w.pre_sorted = off; off = align_up(off + (size_t)w.cap_pre * sizeof(PreItem), 256);
     w.merge_list = off; off = align_up(off + (size_t)num_seqs * 16, 256);
     w.ml = off;         off = align_up(off + (size_t)w.cap_dec * num_q_heads * 2 * 4, 256);
     w.acc = off;        off = align_up(off + (size_t)w.cap_dec * num_q_heads * head_dim * 4, 256);

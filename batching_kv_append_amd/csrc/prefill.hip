@@ -65,10 +65,8 @@ struct PrefillParams {
     const uint4* k_cache;
     const uint4* v_cache;
     const int32_t* table;
-    const int32_t* cu;
-    const int32_t* ctx;
     int32_t* hdr;
-    const int2* items;
+    const PreItem* items;
     int64_t num_blocks;
     int32_t max_blocks, hq, hkv, G, HC;
     int32_t xcd_map;   // 1: head slots % 8 == 0, 2: 8 % head slots == 0, 0: plain
@@ -174,15 +172,20 @@ __global__ __launch_bounds__(64 * NW, A > 128 ? 1 : 2) void prefill_kernel(Prefi
 
     int item, slot;
     prefill_unit((int)blockIdx.x, P.hkv * P.HC, P.xcd_map, item, slot);
-    if (item >= P.hdr[HDR_N_PRE]) return;
-    const int2 it = P.items[item];
-    const int s = it.x, tile = it.y;
+    // The item's record (sequence, lengths) is read together with the
+    // planned count: item is below the list's capacity, so the read is in
+    // bounds either way, and testing both values keeps the two loads in one
+    // round trip.
+    const int n_pre = P.hdr[HDR_N_PRE];
+    const PreItem it = P.items[item];
+    if (item >= n_pre || it.s < 0) return;
+    const int s = it.s, tile = it.tile;
     const int kvh = slot / P.HC;
     const int hc = slot % P.HC;
     const int h = kvh * P.G + hc * HPW + (wave % HPW);
-    const int row0 = P.cu[s];
-    const int qlen = P.cu[s + 1] - row0;
-    const int c = P.ctx[s];
+    const int row0 = it.row0;
+    const int qlen = it.qlen;
+    const int c = it.ctx;
     const int L = c + qlen;
     constexpr int NPB = NW / HPW;  // position blocks per workgroup (snake order across items)
     const int p0 = prefill_block(tile, wave / HPW, (qlen + SPAN - 1) / SPAN) * QW;  // first position of this wave
@@ -538,10 +541,8 @@ hipError_t launch_prefill(const StepArgs& a) {
     p.k_cache = (const uint4*)a.k_cache;
     p.v_cache = (const uint4*)a.v_cache;
     p.table = a.block_table;
-    p.cu = a.cu_seqlens_q;
-    p.ctx = a.context_lens;
     p.hdr = (int32_t*)(ws + a.lay.hdr);
-    p.items = (const int2*)(ws + a.lay.pre_sorted);
+    p.items = (const PreItem*)(ws + a.lay.pre_sorted);
     p.num_blocks = a.num_blocks;
     p.max_blocks = a.max_blocks;
     p.hq = a.num_q_heads;

@@ -493,13 +493,24 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
     const bool has_decode =
         max_q_len < 2 ||
         (int64_t)num_seqs * max_q_len - total_q >= (int64_t)max_q_len - 1;
-    // Chunks-only calls take the 8-wave prefill workgroups (one per compute
-    // unit, every K/V tile shared by 8 waves, P.V a tile late on half of
-    // them); beside a decode the 4-wave ones, which leave the decode more of
-    // each compute unit.
-    a.prefill_waves = (!has_decode && head_dim <= 128) ? 8 : 4;
+    // The prefill overlaps the decode only when the decode's workgroups can
+    // fill the chip beside it: the grid's upper bound (the host sizes' work
+    // items x kv heads x head chunks) at least one per compute unit.  A few
+    // decode rows next to a long chunk would otherwise take compute units
+    // from the prefill's one round of workgroups and leave them idle for most
+    // of it (a 2048-row chunk at 6144 cached keys beside 2 decode rows: 390 us
+    // overlapped, 330 us one after the other).
+    const int G = num_q_heads / num_kv_heads;
+    int64_t dec_wgs = lay.cap_dec * num_kv_heads * (G / kvc::decode_heads_per_wave(G, head_dim));
+    if (!decode_on_mfma(head_dim)) dec_wgs = (dec_wgs + 3) / 4;  // four waves per workgroup
+    const bool side = overlap && has_decode && dec_wgs >= kvc::device_cu_count();
+    // A prefill that has the chip to itself (chunks only, or run before the
+    // decode) takes the 8-wave workgroups (one per compute unit, every K/V
+    // tile shared by 8 waves, P.V a tile late on half of them); beside a
+    // decode the 4-wave ones, which leave the decode more of each unit.
+    a.prefill_waves = (!side && head_dim <= 128) ? 8 : 4;
 
-    return run_step(a, has_decode, overlap, fn);
+    return run_step(a, has_decode, side, fn);
 }
 
 }  // namespace kvc

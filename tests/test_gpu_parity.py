@@ -127,6 +127,17 @@ def test_nonpositive_scale(kvc, orc, a, scale):
           scale=scale)
 
 
+@pytest.mark.parametrize("a", [16, 64, 128, 256])
+def test_prefill_beside_a_full_decode(kvc, orc, a):
+    """Enough decode rows (300) for the decode to fill the chip, so the chunks
+    run beside it on the side stream with the 4-wave prefill workgroups; the
+    small cases above, with a few decode rows, run the prefill first with the
+    8-wave ones."""
+    rng = np.random.default_rng(40 + a)
+    specs = [(int(c), 1) for c in rng.integers(0, 300, 300)] + [(0, 100), (150, 70), (33, 129)]
+    _case(kvc, orc, f"overlap_a{a}", specs, 8, 2, a, 16)
+
+
 def _rising_keys(wl, top, seed=5):
     """Every K row of every sequence becomes s_p * w: one fixed unit direction w
     per kv head and a magnitude s_p rising linearly with the position p up to

@@ -3,7 +3,8 @@
 Three back-to-back calls on one non-default stream reuse one workspace and
 one output tensor.  Each call mixes a long prefill chunk (2048 rows at a
 cached length of 3072 and more, so the prefill on the library's side stream
-outlasts the decode) with decode rows.  After each call the output is copied
+outlasts the decode) with 120 decode rows (enough for the decode to fill the
+chip, the condition for the side stream).  After each call the output is copied
 to pinned host memory with a non-blocking copy on the same stream.  The test
 then waits on one event recorded on that stream, never on the device, and
 compares every row of every call with the oracle.  If a call returned before
@@ -38,7 +39,9 @@ def kvc():
 @pytest.fixture(scope="module")
 def case(orc):
     rng = np.random.default_rng(31)
-    dec_ctx = [int(c) for c in rng.integers(100, 2000, 12)]
+    # enough decode sequences that the decode fills the chip, so the library
+    # runs the prefill on its side stream
+    dec_ctx = [int(c) for c in rng.integers(100, 2000, 120)]
     specs = [(3072, CALLS * CHUNK)] + [(c, CALLS) for c in dec_ctx]
     wl = W.make_step_workload("streams", specs, num_q_heads=HQ, num_kv_heads=HKV, head_dim=A,
                               block_size=BS, seed=31)

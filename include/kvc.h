@@ -48,7 +48,10 @@
  *   Heads     Query head h reads kv head h / (num_q_heads / num_kv_heads).
  *   Streams   `stream` is a hipStream_t (NULL = the null stream).  Device
  *             work is enqueued asynchronously, in stream order.  When a step
- *             has both prefill chunks and decode rows,
+ *             has prefill chunks and enough decode rows to fill the GPU
+ *             (judged from the host sizes: the decode's work items, kv heads
+ *             and head chunks against the compute units; otherwise the
+ *             prefill simply runs first on `stream`),
  *             kvc_paged_attention_varlen runs the prefill kernel on an
  *             internal side stream that belongs to `stream` (one per caller
  *             stream and device, created on first use, default priority),

@@ -496,10 +496,11 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
     // The prefill overlaps the decode only when the decode's workgroups can
     // fill the chip beside it: the grid's upper bound (the host sizes' work
     // items x kv heads x head chunks) at least one per compute unit.  A few
-    // decode rows next to a long chunk would otherwise take compute units
-    // from the prefill's one round of workgroups and leave them idle for most
-    // of it (a 2048-row chunk at 6144 cached keys beside 2 decode rows: 390 us
-    // overlapped, 330 us one after the other).
+    // decode rows next to a long chunk would otherwise hold compute units
+    // that the prefill's single round of workgroups needs, and the workgroups
+    // waiting for them finish that much later (a 2048-row chunk at 6144
+    // cached keys beside 2 decode rows: 390 us overlapped, 330 us one after
+    // the other).
     const int G = num_q_heads / num_kv_heads;
     int64_t dec_wgs = lay.cap_dec * num_kv_heads * (G / kvc::decode_heads_per_wave(G, head_dim));
     if (!decode_on_mfma(head_dim)) dec_wgs = (dec_wgs + 3) / 4;  // four waves per workgroup

@@ -851,6 +851,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "ms_per_step_kernel_events_pass": elapsed_events * 1e3 / args.steps,
         "ms_per_step_cold_cache": float(np.median(cold_ms)),
+        "ms_per_step_cold_cache_p90": float(np.percentile(cold_ms, 90)),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the pages' workloads)",
         "config": {"workload": desc, "name": args.workload, "calls_per_step": len(calls),

@@ -24,7 +24,7 @@ struct StepArgs {
     int32_t num_q_heads, num_kv_heads, head_dim, block_size;
     float scale;
     const int32_t* key_start = nullptr;  // left-padded batch: first unpadded key per sequence
-    int32_t prefill_waves = 4;  // prefill workgroup size: 8 on calls without decode rows (head_dim <= 128)
+    int32_t prefill_waves = 4;  // prefill workgroup size: 8 when no decode runs beside it (head_dim <= 128)
     char* ws;  // workspace base
     WsLayout lay;
     hipStream_t stream;

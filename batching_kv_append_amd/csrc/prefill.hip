@@ -24,9 +24,10 @@
 // Work: one workgroup = NW waves = HPW query heads of one kv group x (NW/HPW)
 // blocks of QW = 32 positions; each wave owns one (head, 32 positions).  The
 // blocks of a sequence are dealt to its workgroups in snake order (an early
-// block with a late one), so their causal key ranges even out.  A
-// call with decode rows takes NW = 4: two workgroups per compute unit, which
-// leaves the co-running decode more of each unit.  A call of chunks only
+// block with a late one), so their causal key ranges even out.  A prefill
+// that runs beside a decode takes NW = 4: two workgroups per compute unit,
+// which leaves the co-running decode more of each unit.  One with the chip to
+// itself (a call of chunks only, or one whose few decode rows run after it)
 // takes NW = 8 up to head_dim 128: one workgroup per compute unit, two waves
 // per SIMD, so every K/V tile brought into the unit feeds 8 waves instead of
 // 4, and waves 4..7 (the second wave of each SIMD) run P.V one tile late, so
@@ -137,7 +138,7 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
 
 // NW = 4: two workgroups per compute unit (one for head_dim 256, whose
 // accumulators and Q^T operand double: 128 KiB of LDS, one wave per SIMD).
-// NW = 8 (calls without decode rows, head_dim <= 128): one workgroup per
+// NW = 8 (no decode beside it, head_dim <= 128): one workgroup per
 // compute unit, two waves per SIMD, each K/V tile fetched once for 8 waves,
 // and the second wave of each SIMD runs P.V one tile late.
 template <int A, int BS, int HPW, int NW>

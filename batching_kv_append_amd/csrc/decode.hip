@@ -543,16 +543,17 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // The two-group kernel is held to two waves per SIMD (at most 256 VGPRs; it
 // fits in 228 without spills): left free it takes about 300 and runs one wave
 // per SIMD, too few loads in flight for a memory-bound kernel.  Head_dim 256
-// takes one group only (two would spill): its accumulators and operands fill
-// about 350 registers, one wave per SIMD, and 32 heads on one kv head run as
-// two head chunks whose workgroups share an XCD (the second reads K/V from
-// its L2).
+// runs one wave per SIMD (about 320 registers with one group, 480 with two,
+// its V rows requested only once the K rows are in LDS so the two staging
+// sets are never live together); with 4-token blocks it takes one group, and
+// 32 heads on one kv head then run as two head chunks whose workgroups share
+// an XCD (the second reads K/V from its L2).
 // MASKED (the left-padded batch): keys below key_start[s] are padding.  They
 // are still read (a padded batch streams every position), their scores are
 // excluded by select and their V rows are zeroed, so whatever the padding
 // holds has weight exactly 0.
 template <int A, int BS, int NG, bool MASKED>
-__global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(DecodeParams P) {
+__global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_kernel(DecodeParams P) {
     static_assert(A == 64 || A == 128 || A == 256, "matrix decode: head_dim 64, 128 or 256");
     constexpr int CPR = A / 8;              // 16-byte chunks per row
     constexpr int STEP = 32;                // tokens per matrix step
@@ -761,7 +762,10 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
     // rows as soon as this step's V^T is in LDS, so they are in flight during
     // this step's products and softmax (the load registers are free by then,
     // and the kernel already runs two waves per SIMD).
-    constexpr bool PF = NG == 2;
+    constexpr bool PF = NG == 2 && A <= 128;
+    // Head_dim 256: V rows are requested once this step's K rows are in LDS,
+    // so the K and V staging registers are never live together.
+    constexpr bool SPLIT = A == 256;
     // Wait here for everything requested so far (the table slice and the Q^T
     // operand, whose loads are conditional), so the loop's waits count only
     // its own K/V loads.
@@ -777,16 +781,9 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         const int tc_next = tc + STEP;
         if (!PF) {
             load_k(tc);
-            load_v(tc);
+            if (!SPLIT) load_v(tc);
         }
         const bool padded = MASKED && tc < kstart;  // some key of this step is padding
-        if (padded) {
-#pragma unroll
-            for (int hh = 0; hh < NVG; ++hh)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (tc + 4 * (lr + VPL * hh) + j < kstart) vb[hh][j] = make_uint4(0, 0, 0, 0);
-        }
 
         // K rows into this wave's tile ([row][chunk ^ row % CPR]), then the
         // A operands: lane (g, col) of block b, step ks takes chunk 4 ks + g
@@ -796,6 +793,14 @@ __global__ __launch_bounds__(256, NG == 2 ? 2 : 1) void decode_mfma_kernel(Decod
         for (int j = 0; j < NKL; ++j) {
             const int r = RPL * j + lr;
             vt[r * CPR + (lc ^ (r % CPR))] = kst[j];
+        }
+        if (!PF && SPLIT) load_v(tc);
+        if (padded) {
+#pragma unroll
+            for (int hh = 0; hh < NVG; ++hh)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (tc + 4 * (lr + VPL * hh) + j < kstart) vb[hh][j] = make_uint4(0, 0, 0, 0);
         }
         uint4 kb[2][KS];
 #pragma unroll
@@ -1106,7 +1111,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
 
 template <int A, int BS, bool MASKED>
 void launch_decode_mfma(const StepArgs& a, const DecodeParams& p, bool two, int grid) {
-    if constexpr (A <= 128) {  // head_dim 256: one column group (registers)
+    if constexpr (A <= 128 || BS == 16) {  // head_dim 256, 4-token blocks: one group (registers)
         if (two) {
             hipLaunchKernelGGL((decode_mfma_kernel<A, BS, 2, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
             return;
@@ -1132,9 +1137,12 @@ void launch_decode_gw(const StepArgs& a, const DecodeParams& p, int GW, int grid
 
 }  // namespace
 
-int decode_heads_per_wave(int G, int head_dim) {
-    if (decode_on_mfma(head_dim)) {  // matrix path: 32 when G is a multiple of 32 (two column
-        if (G % 32 == 0 && head_dim <= 128) return 32;  // groups), else the largest divisor of G <= 16
+// Matrix path: 32 when G is a multiple of 32 (two column groups; not at
+// head_dim 256 with 4-token blocks, whose table slice leaves no registers for
+// them), else the largest divisor of G up to 16.
+int decode_heads_per_wave(int G, int head_dim, int block_size) {
+    if (decode_on_mfma(head_dim)) {
+        if (G % 32 == 0 && (head_dim <= 128 || block_size == 16)) return 32;
         for (int gw = G < 16 ? G : 16; gw > 1; --gw)
             if (G % gw == 0) return gw;
         return 1;
@@ -1181,7 +1189,7 @@ hipError_t launch_prep(const StepArgs& a, bool with_append) {
 hipError_t launch_decode(const StepArgs& a) {
     char* ws = a.ws;
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int GW = decode_heads_per_wave(G, a.head_dim);
+    const int GW = decode_heads_per_wave(G, a.head_dim, a.block_size);
     DecodeParams p;
     p.q = (const uint16_t*)a.q;
     p.out = (uint16_t*)a.out;

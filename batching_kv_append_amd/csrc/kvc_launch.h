@@ -60,7 +60,7 @@ hipError_t launch_prefill(const StepArgs& a);
 int device_cu_count();
 // Query heads per decode wave for a group ratio G (the kv head's heads are cut
 // into G / that many head chunks).
-int decode_heads_per_wave(int G, int head_dim);
+int decode_heads_per_wave(int G, int head_dim, int block_size);
 
 // Argument checks and launches of one step, shared by the entry points that
 // run it (kvc_paged_attention_varlen and its variants): `fn` names the entry

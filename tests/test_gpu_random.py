@@ -1,5 +1,6 @@
 """Seeded random shapes against the oracle: many small ragged batches that mix
-decode rows, prompt chunks and empty rows, over the supported head groupings
+decode rows, prompt chunks and empty rows, chunks-only calls and wide decode
+batches with a few chunks, over the supported head groupings
 (G = 1, 2 or a multiple of 4), block sizes 4 and 16 and head dims 16, 64, 128
 and 256,
 with context lengths drawn around block, tile, partition and work-item boundaries.  Same
@@ -61,11 +62,30 @@ def _chunks_only_case(i):
                 hkv=hkv, a=a, bs=bs, seed=4000 + i)
 
 
+def _wide_case(i):
+    """300-500 sequences on 2 kv heads, nearly all decode rows plus a few
+    chunks: enough decode work (at least one workgroup per compute unit) for
+    the prefill to run beside it on the side stream."""
+    rng = np.random.default_rng(5000 + i)
+    g = int(rng.choice([1, 4, 8, 32]))
+    hkv = 2
+    a = int(rng.choice([16, 64, 128, 256]))
+    bs = int(rng.choice([4, 16]))
+    n = int(rng.integers(300, 500))
+    specs = [(int(rng.integers(0, 600)), 1 if rng.random() < 0.97 else int(rng.integers(2, 200)))
+             for _ in range(n)]
+    specs[0] = (specs[0][0], 64)
+    return dict(name=f"wide{i:02d}_g{g}_hkv{hkv}_a{a}_bs{bs}_n{n}", specs=specs, hq=g * hkv,
+                hkv=hkv, a=a, bs=bs, seed=6000 + i)
+
+
 CASES = [_case(i) for i in range(N_CASES)]
 # head dims 64 and 256 (the matrix decode and prefill instances of those sizes)
 CASES += [_case(i, dims=(64, 256)) for i in range(N_CASES, N_CASES + 12)]
 # chunks only (the 8-wave prefill with P.V a tile late on half the waves)
 CASES += [_chunks_only_case(i) for i in range(10)]
+# wide decode batches with chunks (the prefill beside the decode)
+CASES += [_wide_case(i) for i in range(8)]
 
 
 @pytest.fixture(scope="module")

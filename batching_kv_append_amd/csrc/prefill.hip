@@ -487,24 +487,39 @@ __global__ __launch_bounds__(64 * NW, A > 128 ? 1 : 2) void prefill_kernel(Prefi
     if (bad) atomicOr(P.hdr + HDR_FLAGS, FLAG_BAD_BLOCK);
 
     // ---- normalise and store ------------------------------------------------
-    const int pos = p0 + col;
+    // The wave's 32 output rows go out through LDS (the V tile buffers, free
+    // once every wave is past its last P.V): each lane writes its 8-byte
+    // pieces of its column's row (16-byte chunks XOR-swizzled by row), then
+    // the wave stores whole rows, CPR lanes x 16 B each, so every global
+    // store instruction writes complete 128-byte lines instead of 16-byte
+    // pieces of 32 rows.  Rows past the chunk are not stored.
+    constexpr int SWZ = CPR < 16 ? CPR : 16;    // chunk swizzle period
+    constexpr int ORPI = 64 / CPR;              // rows per store instruction
+    static_assert(NW * QW * A * 2 <= (int)sizeof(sV), "output rows fit the V tiles");
     const float lw = (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-    const float lt = halves_sum(lw);
-    if (pos < qlen) {
-        const float inv = 1.f / lt;
-        uint16_t* orow = P.out + ((int64_t)(row0 + pos) * P.hq + h) * A;
+    const float inv = 1.f / halves_sum(lw);  // columns past the chunk: never stored
+    __syncthreads();  // every wave is done with the V tiles
+    char* ob = reinterpret_cast<char*>(&sV[0][0]) + wave * (QW * A * 2);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d = dt * 32 + 8 * rg + 4 * hi;
-                if (d < A) {
-                    uint2 v;
-                    v.x = pack_bf16x2(o[dt][rg * 4 + 0] * inv, o[dt][rg * 4 + 1] * inv);
-                    v.y = pack_bf16x2(o[dt][rg * 4 + 2] * inv, o[dt][rg * 4 + 3] * inv);
-                    *reinterpret_cast<uint2*>(orow + d) = v;
-                }
+        for (int rg = 0; rg < 4; ++rg) {
+            const int d = dt * 32 + 8 * rg + 4 * hi;
+            if (d < A) {
+                uint2 v;
+                v.x = pack_bf16x2(o[dt][rg * 4 + 0] * inv, o[dt][rg * 4 + 1] * inv);
+                v.y = pack_bf16x2(o[dt][rg * 4 + 2] * inv, o[dt][rg * 4 + 3] * inv);
+                const int ch = (d >> 3) ^ (col % SWZ);
+                *reinterpret_cast<uint2*>(ob + col * (A * 2) + ch * 16 + hi * 8) = v;
             }
+        }
+#pragma unroll
+    for (int i = 0; i < QW / ORPI; ++i) {
+        const int r = i * ORPI + lane / CPR;  // row of the wave's block
+        const int c = lane % CPR;             // 16-byte chunk: dims 8c .. 8c+7
+        const uint4 v = *reinterpret_cast<const uint4*>(ob + r * (A * 2) + ((c ^ (r % SWZ)) * 16));
+        if (p0 + r < qlen)
+            *reinterpret_cast<uint4*>(P.out + ((int64_t)(row0 + p0 + r) * P.hq + h) * A + c * 8) = v;
     }
 }
 

@@ -100,10 +100,11 @@ def test_small(kvc, orc, name, specs, hq, hkv, a, bs):
     _case(kvc, orc, name, specs, hq, hkv, a, bs)
 
 
-def test_planner_beyond_its_lds_cache(kvc, orc):
-    """More sequences (2500) and more prefill work items (4200) than the
-    planner keeps in LDS (2048 of each), in shuffled order, so both its cached
-    and its global-memory paths place work."""
+def test_planner_over_several_passes(kvc, orc):
+    """More sequences (2500) and prefill work items (4200) than the planner's
+    1024 threads cover in one pass, in shuffled order, so its offsets carry
+    from pass to pass (sequences, decode items, merge descriptors) and the
+    cost sort spans several passes over the items."""
     rng = np.random.default_rng(11)
     specs = [(int(c), 33) for c in rng.integers(0, 40, 2100)]
     specs += [(int(c), 1) for c in rng.integers(0, 1500, 400)]

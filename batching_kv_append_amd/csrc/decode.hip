@@ -308,6 +308,9 @@ struct DecodeParams {
 
 constexpr float NEG_BIG = -1.0e30f;  // "no key yet": finite, so exp2(NEG_BIG - m) == 0
 
+// Vector-ALU decode partials, one wave per 256-token partition.  Written for
+// any head size; launched for head_dim 16, whose 32-byte rows fall short of
+// the matrix decode's 32-dim step.
 template <int A, int BS, int GW>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     constexpr int LPR = A / 8;      // lanes per token row (16 B per lane)

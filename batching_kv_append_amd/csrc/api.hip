@@ -502,9 +502,8 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
     // cached keys beside 2 decode rows: 390 us overlapped, 330 us one after
     // the other).
     const int G = num_q_heads / num_kv_heads;
-    int64_t dec_wgs =
+    const int64_t dec_wgs =
         lay.cap_dec * num_kv_heads * (G / kvc::decode_heads_per_wave(G, head_dim, block_size));
-    if (!decode_on_mfma(head_dim)) dec_wgs = (dec_wgs + 3) / 4;  // four waves per workgroup
     const bool side = overlap && has_decode && dec_wgs >= kvc::device_cu_count();
     // A prefill that has the chip to itself (chunks only, or run before the
     // decode) takes the 8-wave workgroups (one per compute unit, every K/V

@@ -6,8 +6,8 @@
 // decode stage is limited by memory access; clvsit.github.io AWS SageMaker
 // page: every step moves the parameters and the cache into the compute
 // units).  The kernels therefore aim at HBM bandwidth:
-//   * a sequence's context is cut into pieces of at most decode_part(head_dim)
-//     tokens (split-K), a cut that depends only on its own length, so even a
+//   * a sequence's context is cut into pieces of at most DECODE_PART tokens
+//     (split-K), a cut that depends only on its own length, so even a
 //     short batch of long contexts yields thousands of independent pieces of
 //     work;
 //     the partial softmax states are combined by an exact log-sum-exp merge
@@ -17,14 +17,12 @@
 //     cover whole 128-byte lines;
 //   * the GW query heads that share a kv head (GQA, e2hang/Notes "MQA与GQA")
 //     are served from one read of K/V;
-//   * head_dims 64, 128 and 256 (decode_mfma_kernel): a sequence is cut into
-//     ceil(L / 4096) work items of equal length, and a workgroup takes one
-//     item of one (sequence, kv head, head chunk), a quarter of it per wave
-//     (at most one 1024-token partition), scores and P.V on bf16 MFMA; the
-//     four states are combined in LDS, so split-K partials (and the merge)
-//     exist per item;
-//   * head_dim 16 (decode_kernel): one wave per 256-token
-//     partition, dot products reduced across the lanes of a token row.
+//   * every head size (16, 64, 128, 256) runs decode_mfma_kernel: a sequence
+//     is cut into ceil(L / 4096) work items of equal length, and a workgroup
+//     takes one item of one (sequence, kv head, head chunk), a quarter of it
+//     per wave (at most one 1024-token partition), scores and P.V on bf16
+//     MFMA; the four states are combined in LDS, so split-K partials (and the
+//     merge) exist per item.
 // The planning kernel lists the work items on the device, longest pieces
 // first, so the host needs no copy of the lengths, and the hardware
 // dispatcher hands the next workgroup to whichever compute unit frees up
@@ -43,15 +41,13 @@ namespace {
 constexpr int PLAN_THREADS = 1024;
 
 constexpr int COST_BUCKETS = 1024;  // prefill cost histogram (key tiles, clamped)
-constexpr int DEC_BUCKETS = DECODE_PART_MFMA / 32;  // decode order: 32-token steps per wave
+constexpr int DEC_BUCKETS = DECODE_PART / 32;  // decode order: 32-token steps per wave
 
 struct PrepParams {
     // planning
     const int32_t* cu;
     const int32_t* ctx;
     int32_t num_seqs, total_q, max_q_len, max_context_len, span;
-    int32_t gp;     // decode partitions per work item
-    int32_t dpart;  // decode partition length (tokens)
     int64_t cap_dec, cap_pre;
     int32_t* hdr;
     int2* dec_items;
@@ -95,7 +91,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     const int32_t* __restrict__ cu = P.cu;
     const int32_t* __restrict__ ctx = P.ctx;
     const int32_t num_seqs = P.num_seqs, total_q = P.total_q, max_q_len = P.max_q_len;
-    const int32_t max_context_len = P.max_context_len, span = P.span, gp = P.gp, dpart = P.dpart;
+    const int32_t max_context_len = P.max_context_len, span = P.span;
     const int64_t cap_dec = P.cap_dec, cap_pre = P.cap_pre;
     int32_t* hdr = P.hdr;
     int2* dec_items = P.dec_items;
@@ -143,11 +139,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     // of the launch.
     auto decode_items = [&](int c, int& bucket) -> int {
         const int L = c + 1;
-        if (gp == 1) {
-            bucket = 0;
-            return (L + dpart - 1) / dpart;
-        }
-        const int ng = (L + gp * dpart - 1) / (gp * dpart);
+        constexpr int gp = DECODE_GROUP;
+        const int ng = (L + gp * DECODE_PART - 1) / (gp * DECODE_PART);
         const int per_wave = ((L + gp * ng - 1) / (gp * ng) + 31) / 32;  // in 32-token steps
         bucket = min(per_wave, DEC_BUCKETS) - 1;
         return ng;
@@ -308,205 +301,8 @@ struct DecodeParams {
 
 constexpr float NEG_BIG = -1.0e30f;  // "no key yet": finite, so exp2(NEG_BIG - m) == 0
 
-// Vector-ALU decode partials, one wave per 256-token partition.  Written for
-// any head size; launched for head_dim 16, whose 32-byte rows fall short of
-// the matrix decode's 32-dim step.
-template <int A, int BS, int GW>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
-    constexpr int LPR = A / 8;      // lanes per token row (16 B per lane)
-    constexpr int RPL = 64 / LPR;   // token rows per load instruction
-    constexpr int NL = (A == 128) ? 8 : (A == 256) ? 4 : 2;  // loads per chunk
-    constexpr int CH = RPL * NL;    // tokens per chunk
-    constexpr int DP = DECODE_PART_VALU;  // partition length
-    constexpr int NT = DP / BS;           // table entries per partition (<= 64)
-    constexpr bool UNIFORM_BLOCK = (BS % RPL) == 0;  // one block per load instruction
-    static_assert(DP % CH == 0, "chunk must divide the partition");
-    static_assert(NT <= 64, "table slice must fit one VGPR");
-
-    const int lane = threadIdx.x & 63;
-    const int r = lane / LPR;
-    const int c8 = lane % LPR;
-    const int64_t n_units = (int64_t)P.hdr[HDR_N_DEC] * P.hkv * P.HC;
-    // One wave per work unit; the grid covers the host-side upper bound and
-    // waves past the planned count leave at once.  The unit index comes from
-    // the launch coordinates only, so it is uniform by construction.
-    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (u >= n_units) return;
-    {
-        const int hc = u % P.HC;
-        const int kvh = (u / P.HC) % P.hkv;
-        const int item = u / (P.HC * P.hkv);
-        const int2 it = P.items[item];
-        const int s = it.x, part = it.y;
-        const int L = P.ctx[s] + 1;
-        const int row = P.cu[s];
-        const int nparts = (L + DP - 1) / DP;
-        const int t0 = part * DP;
-        const int t1 = min(L, t0 + DP);
-        const int h0 = kvh * P.G + hc * GW;
-
-        // table slice of this partition: lane i holds entry (t0 / BS + i)
-        const int lb0 = t0 / BS;
-        const int nlb = (t1 - t0 + BS - 1) / BS;
-        int tbl = -1, short_tbl = 0;  // short_tbl: a needed block is past the table row
-        if (lane < nlb && lane < NT) {
-            const int64_t lb = lb0 + lane;
-            if (lb < P.max_blocks) tbl = P.table[(int64_t)s * P.max_blocks + lb];
-            else short_tbl = 1;
-        }
-
-        // q for GW heads, pre-scaled into the exp2 domain
-        float qf[GW][8];
-#pragma unroll
-        for (int g = 0; g < GW; ++g) {
-            const uint4 qq = *reinterpret_cast<const uint4*>(
-                P.q + (((int64_t)row * P.hq + h0 + g) * A + c8 * 8));
-            const uint32_t w[4] = {qq.x, qq.y, qq.z, qq.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                qf[g][2 * e] = bf_lo(w[e]) * P.scale_log2;
-                qf[g][2 * e + 1] = bf_hi(w[e]) * P.scale_log2;
-            }
-        }
-        float m[GW], l[GW], acc[GW][8];
-#pragma unroll
-        for (int g = 0; g < GW; ++g) {
-            m[g] = NEG_BIG;
-            l[g] = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-        }
-        int bad = 0;
-
-        for (int tc = t0; tc < t1; tc += CH) {
-            uint4 kr[NL], vr[NL];
-            bool ok[NL];
-#pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                const int t = tc + j * RPL + r;
-                int blk;
-                if constexpr (UNIFORM_BLOCK) {
-                    blk = __builtin_amdgcn_readlane(tbl, ((tc + j * RPL) / BS - lb0));
-                } else {
-                    blk = __shfl(tbl, (t / BS - lb0) & 63, 64);
-                }
-                const bool in_range = blk >= 0 && blk < P.num_blocks;
-                ok[j] = (t < t1) && in_range;
-                bad |= (t < t1) && !in_range;
-                kr[j] = make_uint4(0, 0, 0, 0);
-                vr[j] = make_uint4(0, 0, 0, 0);
-                if (ok[j]) {
-                    const int64_t off =
-                        (((int64_t)blk * P.hkv + kvh) * BS + (t % BS)) * LPR + c8;
-                    kr[j] = P.k_cache[off];
-                    vr[j] = P.v_cache[off];
-                }
-            }
-            float sc[NL][GW];
-#pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                const uint32_t w[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
-                float kf[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kf[2 * e] = bf_lo(w[e]);
-                    kf[2 * e + 1] = bf_hi(w[e]);
-                }
-#pragma unroll
-                for (int g = 0; g < GW; ++g) {
-                    float d = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) d = fmaf(qf[g][e], kf[e], d);
-                    d = group_sum<LPR>(d);
-                    sc[j][g] = ok[j] ? d : -INFINITY;
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < GW; ++g) {
-                float mx = sc[0][g];
-#pragma unroll
-                for (int j = 1; j < NL; ++j) mx = fmaxf(mx, sc[j][g]);
-                const float m_new = fmaxf(m[g], mx);
-                const float alpha = __builtin_amdgcn_exp2f(m[g] - m_new);
-                l[g] *= alpha;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
-                m[g] = m_new;
-            }
-#pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-                float vf[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vf[2 * e] = bf_lo(w[e]);
-                    vf[2 * e + 1] = bf_hi(w[e]);
-                }
-#pragma unroll
-                for (int g = 0; g < GW; ++g) {
-                    const float p = __builtin_amdgcn_exp2f(sc[j][g] - m[g]);
-                    l[g] += p;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
-                }
-            }
-        }
-        // a block past the table reads as id -1: reported as a short table
-        if (__any(short_tbl)) {
-            if (lane == 0) set_flag(P.hdr, FLAG_TABLE_SHORT);
-        } else if (__any(bad)) {
-            if (lane == 0) set_flag(P.hdr, FLAG_BAD_BLOCK);
-        }
-
-        // merge the RPL row groups of the wave (lanes c8, c8+LPR, ...)
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-            for (int g = 0; g < GW; ++g) {
-                const float m2 = shfl_xor_f(m[g], off);
-                const float l2 = shfl_xor_f(l[g], off);
-                const float M = fmaxf(m[g], m2);
-                const float a1 = __builtin_amdgcn_exp2f(m[g] - M);
-                const float a2 = __builtin_amdgcn_exp2f(m2 - M);
-                l[g] = l[g] * a1 + l2 * a2;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[g][e] = acc[g][e] * a1 + shfl_xor_f(acc[g][e], off) * a2;
-                m[g] = M;
-            }
-        }
-
-        if (lane < LPR) {
-            if (nparts == 1) {
-#pragma unroll
-                for (int g = 0; g < GW; ++g) {
-                    const float inv = 1.f / l[g];
-                    uint4 o;
-                    o.x = pack_bf16x2(acc[g][0] * inv, acc[g][1] * inv);
-                    o.y = pack_bf16x2(acc[g][2] * inv, acc[g][3] * inv);
-                    o.z = pack_bf16x2(acc[g][4] * inv, acc[g][5] * inv);
-                    o.w = pack_bf16x2(acc[g][6] * inv, acc[g][7] * inv);
-                    *reinterpret_cast<uint4*>(P.out + (((int64_t)row * P.hq + h0 + g) * A + c8 * 8)) = o;
-                }
-            } else {
-#pragma unroll
-                for (int g = 0; g < GW; ++g) {
-                    const int64_t slot = (int64_t)item * P.hq + h0 + g;
-                    float4* dst = reinterpret_cast<float4*>(P.ws_acc + slot * A + c8 * 8);
-                    dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
-                    dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
-                    if (lane == 0) {
-                        P.ws_ml[slot * 2] = m[g];
-                        P.ws_ml[slot * 2 + 1] = l[g];
-                    }
-                }
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Decode partial kernel on the matrix cores (head_dims 64, 128 and 256).
+// Decode partial kernel on the matrix cores (head_dims 16, 64, 128 and 256).
 //
 // Both products of a decode step are small matrix products once the query
 // heads that share a kv head are stacked as columns (up to 16):
@@ -521,6 +317,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
 // column share one running maximum (two lane exchanges per step), so the
 // weights summed by one matrix instruction share one scale.  The VALU work per
 // 32-token step is about 80 instructions, far under the bytes' HBM time.
+// Head_dim 16 is half of one 32-dim step: its K rows sit in the tile padded
+// with 16 zero dims (and the Q^T operand's upper 16 dims are zero), so the
+// same 16x16x32 products serve it.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -557,16 +356,22 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // holds has weight exactly 0.
 template <int A, int BS, int NG, bool MASKED>
 __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_kernel(DecodeParams P) {
-    static_assert(A == 64 || A == 128 || A == 256, "matrix decode: head_dim 64, 128 or 256");
+    static_assert(A == 16 || A == 64 || A == 128 || A == 256, "matrix decode: head_dim 16 to 256");
     constexpr int CPR = A / 8;              // 16-byte chunks per row
     constexpr int STEP = 32;                // tokens per matrix step
-    constexpr int RPL = 64 / CPR;           // whole K rows per load instruction (4 or 8)
+    constexpr int RPL = 64 / CPR;           // whole K rows per load instruction (2 to 32)
     constexpr int NKL = STEP / RPL;         // K load instructions per step
-    constexpr int KS = A / 32;              // 32-dim steps of S^T = K Q^T
+    constexpr int KS = (A + 31) / 32;       // 32-dim steps of S^T = K Q^T
     constexpr int DT = A / 16;              // 16-dim tiles of O^T
-    constexpr int VPL = 64 / CPR;           // 4-token V row groups per load instruction
-    constexpr int NVG = 8 / VPL;            // 4-token V row groups per lane (2, or 1 at head_dim 64)
-    constexpr int DP = DECODE_PART_MFMA;    // partition length: at most one wave's tokens
+    // Head_dim 16: the K tile holds each row zero-padded to one 32-dim step
+    // (chunks 2 and 3 zero), placed past the V^T tile so the zeros stay.
+    constexpr int KCPR = A < 32 ? 4 : CPR;  // 16-byte chunks per K tile row
+    constexpr int KOFF = A < 32 ? A * 4 : 0;  // K tile offset in the wave's tile
+    // 4-token V row groups per load instruction (head_dim 16: lanes 16..63
+    // repeat lanes 0..15, which already cover a 32-token step)
+    constexpr int VPL = A < 32 ? 8 : 64 / CPR;
+    constexpr int NVG = 8 / VPL;            // 4-token V row groups per lane (2, or 1 at head_dim <= 64)
+    constexpr int DP = DECODE_PART;         // partition length: at most one wave's tokens
     constexpr int NT = DP / BS;             // table entries per wave, at most
     constexpr int NTV = (NT + 63) / 64;     // VGPRs holding them (4 for 4-token blocks)
     constexpr float RESCALE_SLACK = 8.0f;   // log2 units: weights stay < 2^8
@@ -578,7 +383,9 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
     // per wave: V^T of one 32-token step, [dim][4 chunks of 8 tokens], 64 B
     // rows; after the loop it holds the wave's accumulators (NG x 8 KiB) for
     // the combine
-    __shared__ uint4 sVt[GP][A * 4 * NG];
+    constexpr int TILE = A < 32 ? A * 4 + 32 * KCPR : A * 4 * NG;  // per wave, 16-byte units
+    static_assert(NG * DT * 64 <= TILE && KOFF + 32 * KCPR <= TILE, "wave tile");
+    __shared__ uint4 sVt[GP][TILE];
     __shared__ float sML[GP][2][16 * NG];  // per wave: column max, column total
     __shared__ int arrived;                        // waves of the group done
 
@@ -586,8 +393,9 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
     const int lane = threadIdx.x & 63;
     const int col = lane & 15;  // head column
     const int g = lane >> 4;    // token group: tokens 4g..4g+3 of each 16-token block
-    const int lr = lane / CPR;  // loads: row (K) or 4-row group (V) of this lane in one instruction
+    const int lr = lane / CPR;  // K loads: row of this lane in one instruction
     const int lc = lane % CPR;  // loads: 16-byte chunk of this lane (dims 8 lc .. 8 lc + 7)
+    const int vr = (A < 32 ? (lane & 15) : lane) / CPR;  // V loads: 4-row group
     // Workgroup -> (work item, kv head, head chunk).  Workgroups go to the 8
     // XCDs round-robin by linear id, each XCD with its own L2; the head
     // chunks of one (item, kv head) are 8 ids apart, so they run on one XCD
@@ -601,6 +409,10 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
     if (threadIdx.x == 0) arrived = 0;
     __syncthreads();  // the only barrier: waves past the sequence leave below
     uint4* vt = &sVt[wave][0];
+    if constexpr (A < 32) {  // the K tile's padding chunks (dims 16..31), zero for good
+        const int r = lane >> 1, ch = 2 + (lane & 1);
+        vt[KOFF + r * KCPR + (ch ^ (r % KCPR))] = make_uint4(0, 0, 0, 0);
+    }
 
     const int GW = P.G / P.HC;  // heads of this wave (<= 16 * NG)
     const int hc = P.HC == 1 ? 0 : (int)((lid >> 3) % P.HC);
@@ -652,7 +464,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             qb[ng][ks] = make_uint4(0, 0, 0, 0);
-            if (16 * ng + col < GW)
+            if (16 * ng + col < GW && (A >= 32 || g * 8 < A))  // head_dim 16: dims 16.. are zero
                 qb[ng][ks] = *reinterpret_cast<const uint4*>(
                     P.q + (((int64_t)row * P.hq + h0 + 16 * ng + col) * A + ks * 32 + g * 8));
         }
@@ -719,14 +531,21 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
     // ---- K: 32 rows, RPL per load, each row whole (CPR lanes x 16 B) --
     // Lane (lr, lc) of load j reads chunk lc of row RPL j + lr; the rows then
     // pass through the wave's LDS tile into the MFMA operand layout.  The
-    // rows of one load share a 16-token block.
+    // rows of one load share a 16-token block (head_dim 16 aside: 32 rows).
     uint4 kst[NKL];
     auto load_k = [&](int tc) __attribute__((always_inline)) {
         const int tv = table_reg(tc);
 #pragma unroll
         for (int j = 0; j < NKL; ++j) {
             const int t = min(tc + RPL * j + lr, t1 - 1);
-            int64_t blk = block_of(tv, t, min(tc + 16 * (RPL * j / 16), t1 - 1));
+            int64_t blk;
+            if constexpr (BS == 16 && RPL > 16) {  // head_dim 16: one load spans both blocks
+                const int64_t b0 = block_of(tv, t, min(tc, t1 - 1));
+                const int64_t b1 = block_of(tv, t, min(tc + 16, t1 - 1));
+                blk = lr >= 16 ? b1 : b0;
+            } else {
+                blk = block_of(tv, t, min(tc + 16 * (RPL * j / 16), t1 - 1));
+            }
             if (blk < 0 || blk >= P.num_blocks) { bad = 1; blk = 0; }
             kst[j] = v_stream(P.k_cache + ((blk * P.hkv + kvh) * BS + t % BS) * CPR + lc);
         }
@@ -735,15 +554,15 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
     // Each load instruction reads VPL whole rows; rows past the end repeat
     // the last row (their weight is 0).  No branch: the two sides of one
     // would load into the same registers, and the second side would wait for
-    // every load in flight.  At head_dim 64 the 8 groups of one instruction
-    // span both 16-token halves of the step, so with 16-token blocks the lane
-    // picks one of the two halves' entries.
+    // every load in flight.  At head_dims 16 and 64 the 8 groups of one
+    // instruction span both 16-token halves of the step, so with 16-token
+    // blocks the lane picks one of the two halves' entries.
     uint4 vb[NVG][4];
     auto load_v = [&](int tc) __attribute__((always_inline)) {
         const int tv = table_reg(tc);
 #pragma unroll
         for (int hh = 0; hh < NVG; ++hh) {
-            const int tg = lr + VPL * hh;
+            const int tg = vr + VPL * hh;
             const int t = min(tc + 4 * tg, t1 - 1);
             int64_t blk;
             if constexpr (BS == 16 && VPL > 4) {
@@ -760,12 +579,14 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
                 vb[hh][j] = v_stream(vp + (min(tc + 4 * tg + j, t1 - 1) - t) * CPR);
         }
     };
-    // With two head groups (PF) the next step's K rows are requested as soon
-    // as this step's are in LDS and the K operands in registers, and its V
-    // rows as soon as this step's V^T is in LDS, so they are in flight during
-    // this step's products and softmax (the load registers are free by then,
-    // and the kernel already runs two waves per SIMD).
-    constexpr bool PF = NG == 2 && A <= 128;
+    // With two head groups (PF), and at head_dim 16, the next step's K rows
+    // are requested as soon as this step's are in LDS and the K operands in
+    // registers, and its V rows as soon as this step's V^T is in LDS, so they
+    // are in flight during this step's products and softmax (the load
+    // registers are free by then, and the kernel already runs two waves per
+    // SIMD; head_dim 16 has registers to spare, and its 2 KiB steps are too
+    // short to keep the memory busy one at a time: GQA batch 52.7 -> 49.5 us).
+    constexpr bool PF = (NG == 2 && A <= 128) || A < 32;
     // Head_dim 256: V rows are requested once this step's K rows are in LDS,
     // so the K and V staging registers are never live together.
     constexpr bool SPLIT = A == 256;
@@ -795,7 +616,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
 #pragma unroll
         for (int j = 0; j < NKL; ++j) {
             const int r = RPL * j + lr;
-            vt[r * CPR + (lc ^ (r % CPR))] = kst[j];
+            vt[KOFF + r * KCPR + (lc ^ (r % KCPR))] = kst[j];
         }
         if (!PF && SPLIT) load_v(tc);
         if (padded) {
@@ -803,7 +624,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
             for (int hh = 0; hh < NVG; ++hh)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (tc + 4 * (lr + VPL * hh) + j < kstart) vb[hh][j] = make_uint4(0, 0, 0, 0);
+                    if (tc + 4 * (vr + VPL * hh) + j < kstart) vb[hh][j] = make_uint4(0, 0, 0, 0);
         }
         uint4 kb[2][KS];
 #pragma unroll
@@ -811,7 +632,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int r = 16 * b + col;
-                kb[b][ks] = vt[r * CPR + ((4 * ks + g) ^ (r % CPR))];
+                kb[b][ks] = vt[KOFF + r * KCPR + ((4 * ks + g) ^ (r % KCPR))];
             }
         if (PF) load_k(tc_next);
 
@@ -832,7 +653,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
         // row load into four 4-byte loads).
 #pragma unroll
         for (int hh = 0; hh < NVG; ++hh) {
-            const int tg = lr + VPL * hh;  // tokens 4 tg .. 4 tg + 3 of the step
+            const int tg = vr + VPL * hh;  // tokens 4 tg .. 4 tg + 3 of the step
             const u16x8_t r0 = __builtin_bit_cast(u16x8_t, vb[hh][0]);
             const u16x8_t r1 = __builtin_bit_cast(u16x8_t, vb[hh][1]);
             const u16x8_t r2 = __builtin_bit_cast(u16x8_t, vb[hh][2]);
@@ -845,7 +666,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
             uint2* vt2 = reinterpret_cast<uint2*>(vt);
             // row d, 16-byte chunk tg % 4 (tokens 4(tg%4).. and 16+4(tg%4)..),
             // half tg / 4 (with 4 groups per instruction: lr and hh)
-            const int gq = VPL == 4 ? lr : (tg & 3);
+            const int gq = VPL == 4 ? vr : (tg & 3);
             const int half = VPL == 4 ? hh : (tg >> 2);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -1015,8 +836,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
 
 // ---------------------------------------------------------------------------
 // Merge kernel: one wave per (decode sequence with several work items, query
-// head); a work item's partial covers one partition group (one partition on
-// the vector-ALU path of head_dim 16).
+// head); a work item's partial covers one partition group.
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // The plan's descriptor carries everything the wave needs, and the (m, l)
 // pairs and accumulators of up to 32 partials are requested together, so a
@@ -1123,34 +943,16 @@ void launch_decode_mfma(const StepArgs& a, const DecodeParams& p, bool two, int 
     hipLaunchKernelGGL((decode_mfma_kernel<A, BS, 1, MASKED>), dim3(grid), dim3(256), 0, a.stream, p);
 }
 
-template <int A, int BS, int GW>
-void launch_decode_t(const StepArgs& a, const DecodeParams& p, int grid) {
-    hipLaunchKernelGGL((decode_kernel<A, BS, GW>), dim3(grid), dim3(256), 0, a.stream, p);
-}
-
-template <int A, int BS>
-void launch_decode_gw(const StepArgs& a, const DecodeParams& p, int GW, int grid) {
-    switch (GW) {
-        case 1: launch_decode_t<A, BS, 1>(a, p, grid); break;
-        case 2: launch_decode_t<A, BS, 2>(a, p, grid); break;
-        case 4: launch_decode_t<A, BS, 4>(a, p, grid); break;
-        default: launch_decode_t<A, BS, 8>(a, p, grid); break;
-    }
-}
-
 }  // namespace
 
-// Matrix path: 32 when G is a multiple of 32 (two column groups; not at
-// head_dim 256 with 4-token blocks, whose table slice leaves no registers for
-// them), else the largest divisor of G up to 16.
+// 32 when G is a multiple of 32 (two column groups; not at head_dim 256 with
+// 4-token blocks, whose table slice leaves no registers for them), else the
+// largest divisor of G up to 16.
 int decode_heads_per_wave(int G, int head_dim, int block_size) {
-    if (decode_on_mfma(head_dim)) {
-        if (G % 32 == 0 && (head_dim <= 128 || block_size == 16)) return 32;
-        for (int gw = G < 16 ? G : 16; gw > 1; --gw)
-            if (G % gw == 0) return gw;
-        return 1;
-    }
-    return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    if (G % 32 == 0 && (head_dim <= 128 || block_size == 16)) return 32;
+    for (int gw = G < 16 ? G : 16; gw > 1; --gw)
+        if (G % gw == 0) return gw;
+    return 1;
 }
 
 hipError_t launch_prep(const StepArgs& a, bool with_append) {
@@ -1164,8 +966,6 @@ hipError_t launch_prep(const StepArgs& a, bool with_append) {
     p.max_q_len = a.max_q_len;
     p.max_context_len = a.max_context_len;
     p.span = prefill_span(G, a.prefill_waves);
-    p.gp = decode_group_parts(G, a.head_dim);
-    p.dpart = decode_part(a.head_dim);
     p.cap_dec = a.lay.cap_dec;
     p.cap_pre = a.lay.cap_pre;
     p.hdr = (int32_t*)(ws + a.lay.hdr);
@@ -1213,38 +1013,41 @@ hipError_t launch_decode(const StepArgs& a) {
     p.G = G;
     p.HC = G / GW;
     p.scale_log2 = a.scale * 1.4426950408889634f;
-    const int gp = decode_group_parts(G, a.head_dim);
     const int64_t units = a.lay.cap_dec * a.num_kv_heads * p.HC;
-    // matrix decode: one workgroup per unit, the head chunks of one (item, kv
-    // head) 8 launch ids apart (so the pairs are padded to a multiple of 8);
-    // vector-ALU decode: one wave per unit
+    // one workgroup per unit, the head chunks of one (item, kv head) 8 launch
+    // ids apart (so the pairs are padded to a multiple of 8)
     const int64_t pairs8 = (a.lay.cap_dec * a.num_kv_heads + 7) / 8 * 8;
-    const int64_t grid64 = gp > 1 ? (p.HC == 1 ? units : pairs8 * p.HC) : (units + 3) / 4;
+    const int64_t grid64 = p.HC == 1 ? units : pairs8 * p.HC;
     if (grid64 <= 0) return hipSuccess;
     if (grid64 > INT32_MAX) return hipErrorInvalidValue;
     const int grid = (int)grid64;
-    if (decode_on_mfma(a.head_dim)) {
-        const bool two = GW > 16;  // 32 heads per wave: two MFMA column groups
-        if (gp != 4) return hipErrorInvalidValue;  // the matrix decode works in partition groups
-        if (a.key_start) {  // the left-padded batch (head_dim 128 only)
-            if (a.head_dim != 128) return hipErrorInvalidValue;
-            if (a.block_size == 16) launch_decode_mfma<128, 16, true>(a, p, two, grid);
-            else launch_decode_mfma<128, 4, true>(a, p, two, grid);
-        } else if (a.head_dim == 128) {
-            if (a.block_size == 16) launch_decode_mfma<128, 16, false>(a, p, two, grid);
-            else launch_decode_mfma<128, 4, false>(a, p, two, grid);
-        } else if (a.head_dim == 64) {
-            if (a.block_size == 16) launch_decode_mfma<64, 16, false>(a, p, two, grid);
+    const bool two = GW > 16;  // 32 heads per wave: two MFMA column groups
+    const bool bs16 = a.block_size == 16;
+    if (a.key_start) {  // the left-padded batch (head_dim 128 only)
+        if (a.head_dim != 128) return hipErrorInvalidValue;
+        if (bs16) launch_decode_mfma<128, 16, true>(a, p, two, grid);
+        else launch_decode_mfma<128, 4, true>(a, p, two, grid);
+        return hipGetLastError();
+    }
+    switch (a.head_dim) {
+        case 16:
+            if (bs16) launch_decode_mfma<16, 16, false>(a, p, two, grid);
+            else launch_decode_mfma<16, 4, false>(a, p, two, grid);
+            break;
+        case 64:
+            if (bs16) launch_decode_mfma<64, 16, false>(a, p, two, grid);
             else launch_decode_mfma<64, 4, false>(a, p, two, grid);
-        } else {
-            if (a.block_size == 16) launch_decode_mfma<256, 16, false>(a, p, two, grid);
+            break;
+        case 128:
+            if (bs16) launch_decode_mfma<128, 16, false>(a, p, two, grid);
+            else launch_decode_mfma<128, 4, false>(a, p, two, grid);
+            break;
+        case 256:
+            if (bs16) launch_decode_mfma<256, 16, false>(a, p, two, grid);
             else launch_decode_mfma<256, 4, false>(a, p, two, grid);
-        }
-    } else {
-        // head_dim 16 takes the vector-ALU decode (one partition per wave)
-        if (a.head_dim != 16) return hipErrorInvalidValue;
-        if (a.block_size == 16) launch_decode_gw<16, 16>(a, p, GW, grid);
-        else launch_decode_gw<16, 4>(a, p, GW, grid);
+            break;
+        default:
+            return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

@@ -1,5 +1,5 @@
-// Device-side helpers shared by the gfx950 kernels: bf16 bit handling,
-// 16-lane DPP row reductions, MFMA operand types and the workspace layout.
+// Device-side helpers shared by the gfx950 kernels: bf16 packing, lane
+// exchanges and the workspace layout.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -24,21 +24,15 @@ enum Flag : int {
     FLAG_CU_SEQLENS = 8
 };
 
-// Decode partition length in tokens: at most what one wave walks.  Fixed per
-// head size (never chosen per batch), so a sequence's partial sums depend only
-// on its own logical positions and the output does not change with batch
-// composition.  The matrix decode (head_dims 64, 128, 256) takes 1024: fewer, longer
-// waves write fewer split-K partials and pay their start-up (table slice, Q
-// operand, first loads) and their combine less often (GQA batch 237 -> 226 us,
-// MQA 141 -> 130 us, mixed step 0.81 -> 0.77 ms against 256).  The vector-ALU
-// decode (the other head sizes) keeps 256.
-constexpr int DECODE_PART_MFMA = 1024;
-constexpr int DECODE_PART_VALU = 256;
-// Head sizes the matrix decode serves (the others take the vector-ALU one).
-constexpr bool decode_on_mfma(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
-constexpr int decode_part(int head_dim) {
-    return decode_on_mfma(head_dim) ? DECODE_PART_MFMA : DECODE_PART_VALU;
-}
+// Decode partition length in tokens: at most what one wave walks.  Fixed
+// (never chosen per batch), so a sequence's partial sums depend only on its
+// own logical positions and the output does not change with batch
+// composition.  1024 rather than 256: fewer, longer waves write fewer split-K
+// partials and pay their start-up (table slice, Q operand, first loads) and
+// their combine less often (head_dim 128: GQA batch 237 -> 226 us, MQA
+// 141 -> 130 us, mixed step 0.81 -> 0.77 ms; head_dim 16 MQA batch with the
+// merge 47 -> 46 us).
+constexpr int DECODE_PART = 1024;
 
 // Prefill: each wave owns one query head and QW consecutive positions; a
 // workgroup of NW waves (4, or 8 on calls without decode rows) covers HPW
@@ -94,25 +88,18 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int prefill_hpw(int G) { return G >= 4 ? 4 : G; }
 inline int prefill_span(int G, int nw = 4) { return PREFILL_QW * (nw / prefill_hpw(G)); }
 
-// Decode partitions per work item: the matrix decode (head_dims 64-256) cuts a
-// sequence into ceil(L / (4 * DECODE_PART_MFMA)) equal items, gives each of a
-// workgroup's four waves a quarter of one item and combines them in LDS, so
-// split-K partials exist per item; the vector-ALU decode (head_dim 16) takes
-// one partition per wave.
-constexpr int DECODE_GROUP = 4;  // partitions per matrix-decode workgroup (its four waves)
-inline int decode_group_parts(int G, int head_dim) {
-    (void)G;
-    return decode_on_mfma(head_dim) ? DECODE_GROUP : 1;
-}
+// Decode partitions per work item: the decode cuts a sequence into
+// ceil(L / (4 * DECODE_PART)) equal items, gives each of a workgroup's four
+// waves a quarter of one item and combines them in LDS, so split-K partials
+// exist per item.
+constexpr int DECODE_GROUP = 4;  // partitions per decode workgroup (its four waves)
 
 inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context_len,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
     WsLayout w{};
     const int G = num_q_heads / num_kv_heads;
-    const int dp = decode_part(head_dim);
-    const int64_t parts = ((int64_t)max_context_len + 1 + dp - 1) / dp;
-    const int gp = decode_group_parts(G, head_dim);
-    w.cap_dec = (int64_t)num_seqs * ((parts + gp - 1) / gp);
+    const int64_t parts = ((int64_t)max_context_len + DECODE_PART) / DECODE_PART;  // of L = ctx + 1
+    w.cap_dec = (int64_t)num_seqs * ((parts + DECODE_GROUP - 1) / DECODE_GROUP);
     w.cap_pre = (int64_t)total_q / prefill_span(G) + num_seqs;  // 4-wave span: the most items
     size_t off = 0;
     w.hdr = off;        off = align_up(off + HDR_WORDS * 4, 256);
@@ -128,13 +115,10 @@ inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context
 
 #ifdef __HIPCC__
 // ---------------------------------------------------------------------------
-// bf16 <-> fp32.  Storage is raw uint16; widening is exact (bf16 is the top
-// half of an fp32).  Narrowing uses the compiler's __bf16 conversion, which is
-// round-to-nearest-even and lowers to v_cvt_pk_bf16_f32 on gfx950.
+// fp32 -> bf16.  Storage is raw uint16.  Narrowing uses the compiler's __bf16
+// conversion, which is round-to-nearest-even and lowers to v_cvt_pk_bf16_f32
+// on gfx950.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     bf16x2_t v;
@@ -150,26 +134,6 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
-}
-
-// Sum over groups of LANES consecutive lanes (LANES in {2, 4, 8, 16, 32}) with
-// DPP row operations (and one lane exchange across rows for 32); every lane of
-// a group ends with the group's sum.
-template <int LANES>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32,
-                  "group size");
-    // quad_perm [1,0,3,2]: swap neighbours
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-    if constexpr (LANES >= 4)  // quad_perm [2,3,0,1]: swap pairs
-        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-    if constexpr (LANES >= 8)  // row_half_mirror: lane i <-> 7-i, joins the two quads
-        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
-    if constexpr (LANES >= 16)  // row_mirror: lane i <-> 15-i, joins the two halves
-        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
-    if constexpr (LANES >= 32)  // lane i <-> i ^ 16: joins two rows of 16
-        x += __shfl_xor(x, 16, 64);
-    return x;
 }
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) {

@@ -32,10 +32,10 @@ def _case(kvc, orc, name, specs, hq, hkv, a, bs, seed=7, scale=None):
     return compare(g, r, what=name)
 
 
-# decode edges: blocks (4, 16), the 256-token partitions of the vector-ALU
-# decode (head_dim 16), and for the matrix decode (head_dims 64-256) the
-# 1024-token wave share and 4096-token work item (a sequence of L = c + 1
-# tokens has ceil(L / 4096) items)
+# decode edges: blocks (4, 16), 32-token steps, short items that leave some
+# of the four waves without keys (one active wave up to L = 32, three at
+# L = 257), the 1024-token wave share and the 4096-token work item (a
+# sequence of L = c + 1 tokens has ceil(L / 4096) items)
 DEC_LENS = [0, 1, 5, 15, 16, 17, 255, 256, 257, 511, 512, 600, 1500, 1023, 1024, 1025, 4095,
             4096, 4097, 8200]
 PRE_SPECS = [(0, 2), (0, 63), (0, 64), (0, 65), (5, 130), (300, 200), (17, 1)]

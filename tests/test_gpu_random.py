@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 24
 # context lengths near the edges the kernels care about: blocks (4, 16),
-# prefill key tiles (64), decode partitions (256 at head_dim 16; 1024 per wave
-# and 4096 per work item for head_dims 64-256)
+# prefill key tiles (64), decode wave shares (1024 per wave) and work items
+# (4096)
 EDGES = [0, 1, 3, 4, 5, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025,
          4095, 4096, 4097]
 

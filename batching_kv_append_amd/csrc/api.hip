@@ -510,6 +510,7 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
     // tile shared by 8 waves, P.V a tile late on half of them); beside a
     // decode the 4-wave ones, which leave the decode more of each unit.
     a.prefill_waves = (!side && head_dim <= 128) ? 8 : 4;
+    a.prefill_beside_decode = side;
 
     return run_step(a, has_decode, side, fn);
 }

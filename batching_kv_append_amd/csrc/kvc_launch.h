@@ -25,6 +25,7 @@ struct StepArgs {
     float scale;
     const int32_t* key_start = nullptr;  // left-padded batch: first unpadded key per sequence
     int32_t prefill_waves = 4;  // prefill workgroup size: 8 when no decode runs beside it (head_dim <= 128)
+    bool prefill_beside_decode = false;  // the prefill runs on the side stream next to the decode
     char* ws;  // workspace base
     WsLayout lay;
     hipStream_t stream;

@@ -523,13 +523,23 @@ __global__ __launch_bounds__(64 * NW, A > 128 ? 1 : 2) void prefill_kernel(Prefi
     }
 }
 
+// Beside the decode at head_dim 128, a compute unit takes at most one prefill
+// workgroup: the launch reserves 20 KiB of unused dynamic LDS, which brings
+// the workgroup's 64 KiB past half of the unit's 160 KiB.  Two of them (464
+// of a SIMD's 512 registers) would leave no room for a decode wave on that
+// unit; one leaves room for a decode workgroup.  Mixed step 0.764 -> 0.756 ms
+// (four runs each, one box).  At head_dim 64 the same cap costs 6 % (0.383 ->
+// 0.406 ms on the same rows) and at 16 it changes nothing, so it is kept to 128.
+constexpr unsigned PREFILL_ONE_PER_CU_PAD = 20 * 1024;
+
 template <int A, int BS, int NW>
 void launch_prefill_nw(const StepArgs& a, const PrefillParams& p, int hpw, dim3 grid) {
     const dim3 block(64 * NW);
+    const unsigned pad = (A == 128 && NW == 4 && a.prefill_beside_decode) ? PREFILL_ONE_PER_CU_PAD : 0u;
     switch (hpw) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<A, BS, 1, NW>), grid, block, 0, a.stream, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<A, BS, 2, NW>), grid, block, 0, a.stream, p); break;
-        default: hipLaunchKernelGGL((prefill_kernel<A, BS, 4, NW>), grid, block, 0, a.stream, p); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<A, BS, 1, NW>), grid, block, pad, a.stream, p); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<A, BS, 2, NW>), grid, block, pad, a.stream, p); break;
+        default: hipLaunchKernelGGL((prefill_kernel<A, BS, 4, NW>), grid, block, pad, a.stream, p); break;
     }
 }
 

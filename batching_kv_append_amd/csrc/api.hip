@@ -508,7 +508,8 @@ int paged_attention(const char* fn, void* out, const void* q, const void* k_new,
     // A prefill that has the chip to itself (chunks only, or run before the
     // decode) takes the 8-wave workgroups (one per compute unit, every K/V
     // tile shared by 8 waves, P.V a tile late on half of them); beside a
-    // decode the 4-wave ones, which leave the decode more of each unit.
+    // decode the 4-wave ones, which leave the decode more of each unit (and
+    // at head_dim 128 at most one of them per unit).
     a.prefill_waves = (!side && head_dim <= 128) ? 8 : 4;
     a.prefill_beside_decode = side;
 

@@ -25,8 +25,9 @@
 // blocks of QW = 32 positions; each wave owns one (head, 32 positions).  The
 // blocks of a sequence are dealt to its workgroups in snake order (an early
 // block with a late one), so their causal key ranges even out.  A prefill
-// that runs beside a decode takes NW = 4: two workgroups per compute unit,
-// which leaves the co-running decode more of each unit.  One with the chip to
+// that runs beside a decode takes NW = 4, which leaves the co-running decode
+// more of each unit (at head_dim 128 one such workgroup per compute unit, by
+// an LDS reservation at launch).  One with the chip to
 // itself (a call of chunks only, or one whose few decode rows run after it)
 // takes NW = 8 up to head_dim 128: one workgroup per compute unit, two waves
 // per SIMD, so every K/V tile brought into the unit feeds 8 waves instead of
@@ -136,7 +137,7 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)const_cast<char*>(p));
 }
 
-// NW = 4: two workgroups per compute unit (one for head_dim 256, whose
+// NW = 4: up to two workgroups per compute unit (one for head_dim 256, whose
 // accumulators and Q^T operand double: 128 KiB of LDS, one wave per SIMD).
 // NW = 8 (no decode beside it, head_dim <= 128): one workgroup per
 // compute unit, two waves per SIMD, each K/V tile fetched once for 8 waves,

@@ -327,6 +327,30 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 
+// Max and sum of x over the lane pairs (l, l ^ 16) and (l, l ^ 32) with the
+// gfx950 row swaps in the VALU, not through the LDS crossbar.
+// v_permlane16_swap trades the odd 16-lane rows of its first operand with the
+// even rows of its second, v_permlane32_swap the upper half-wave of the first
+// with the lower half of the second; swapping x with itself leaves each lane
+// with x of one of the pair in the first result and x of the other in the
+// second (the same two values, in the same order, on both lanes of a pair).
+__device__ __forceinline__ float max_x16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -701,8 +725,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
             }
             float mx = fmaxf(fmaxf(fmaxf(v8[0], v8[1]), fmaxf(v8[2], v8[3])),
                              fmaxf(fmaxf(v8[4], v8[5]), fmaxf(v8[6], v8[7])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            mx = max_x32(max_x16(mx));
             const float cand = pos_scale ? mx * cs : mx;
             const bool grow = cand > m[ng] + RESCALE_SLACK;
             if (__any(grow)) {
@@ -747,8 +770,7 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
     float lt[NG];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
-        lt[ng] = lsum[ng] + __shfl_xor(lsum[ng], 16, 64);
-        lt[ng] += __shfl_xor(lt[ng], 32, 64);
+        lt[ng] = sum_x32(sum_x16(lsum[ng]));
     }
     // normalised bf16 output of column group ng (scaled by inv)
     auto write_out = [&](int ng, const f32x4_t (&acc)[DT], float inv) {

@@ -132,7 +132,8 @@ def test_nonpositive_scale(kvc, orc, a, scale):
 @pytest.mark.parametrize("a", [16, 64, 128, 256])
 def test_prefill_beside_a_full_decode(kvc, orc, a):
     """Enough decode rows (300) for the decode to fill the chip, so the chunks
-    run beside it on the side stream with the 4-wave prefill workgroups; the
+    run beside it on the side stream with the 4-wave prefill workgroups (at
+    most one per compute unit at head_dim 128, by an LDS reservation); the
     small cases above, with a few decode rows, run the prefill first with the
     8-wave ones."""
     rng = np.random.default_rng(40 + a)

@@ -80,7 +80,13 @@ SMALL = [
     ("bound_chunks_only", [(50, 4), (300, 2)], 8, 2, 128, 16),
     ("bound_empty_seq", [(50, 4), (300, 0), (10, 3), (2000, 1)], 8, 2, 128, 16),
     ("a16_bound_one_decode", [(9, 3), (40, 1)], 2, 1, 16, 4),
-    # head dims 64 and 256, block sizes 4 and 16, G = 1, 4 and 32
+    # head dims 16, 64 and 256, block sizes 4 and 16, G = 1, 4 and 32 (at 16 a
+    # K row fills half of one 32-dim step and a 32-row K load spans two blocks)
+    ("a16_decode_g1_bs16", [(c, 1) for c in DEC_LENS], 4, 4, 16, 16),
+    ("a16_decode_g4_bs4", [(c, 1) for c in DEC_LENS], 8, 2, 16, 4),
+    ("a16_decode_g32", [(c, 1) for c in DEC_LENS], 32, 1, 16, 16),
+    ("a16_decode_g32_bs4", [(c, 1) for c in DEC_LENS], 64, 2, 16, 4),
+    ("a16_mixed_g32_bs16", MIXED_SPECS, 32, 1, 16, 16),
     ("a64_decode_g1_bs16", [(c, 1) for c in DEC_LENS], 4, 4, 64, 16),
     ("a64_decode_g4_bs4", [(c, 1) for c in DEC_LENS], 8, 2, 64, 4),
     ("a64_decode_g32", [(c, 1) for c in DEC_LENS[:9]], 32, 1, 64, 16),

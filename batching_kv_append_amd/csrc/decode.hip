@@ -351,6 +351,35 @@ __device__ __forceinline__ float sum_x32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Max and sum over the whole wave, every lane ending with the result: DPP
+// row operations inside each 16-lane row (swap neighbours, swap pairs, then
+// row_half_mirror and row_mirror, each of which meets a lane of the half that
+// does not yet hold its total), then the two row swaps above.  Each step adds
+// or compares the same two values on both lanes it pairs, so every lane holds
+// the same bits.
+__device__ __forceinline__ float dpp_f(float x, int ctrl) {
+    switch (ctrl) {  // the control word must be a constant
+        case 0xB1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+        case 0x4E: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+        case 0x141: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+        default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+    }
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f(x, 0xB1));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f(x, 0x4E));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f(x, 0x141));  // row_half_mirror
+    x = fmaxf(x, dpp_f(x, 0x140));  // row_mirror
+    return max_x32(max_x16(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f(x, 0xB1);
+    x += dpp_f(x, 0x4E);
+    x += dpp_f(x, 0x141);
+    x += dpp_f(x, 0x140);
+    return sum_x32(sum_x16(x));
+}
+
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -919,8 +948,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
             }
         }
         float cm = ml.x;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, shfl_xor_f(cm, off));
+        cm = wave_max(cm);
         const float Mn = fmaxf(M, cm);
         const float a = __builtin_amdgcn_exp2f(M - Mn);
         den *= a;
@@ -929,8 +957,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams P) {
         M = Mn;
         const float w = lane < n ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
         float wl = w * ml.y;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) wl += shfl_xor_f(wl, off);
+        wl = wave_sum(wl);
         den += wl;
 #pragma unroll
         for (int p = 0; p < CH; ++p) {

@@ -136,10 +136,6 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
 }
 
-__device__ __forceinline__ float shfl_xor_f(float x, int mask) {
-    return __shfl_xor(x, mask, 64);
-}
-
 __device__ __forceinline__ void set_flag(int32_t* hdr, int flag) {
     atomicOr(hdr + HDR_FLAGS, flag);
 }

@@ -138,12 +138,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(PrepParams P) {
     // and items with longer quarters run first, so short ones fill the end
     // of the launch.
     auto decode_items = [&](int c, int& bucket) -> int {
-        const int L = c + 1;
-        constexpr int gp = DECODE_GROUP;
-        const int ng = (L + gp * DECODE_PART - 1) / (gp * DECODE_PART);
-        const int per_wave = ((L + gp * ng - 1) / (gp * ng) + 31) / 32;  // in 32-token steps
-        bucket = min(per_wave, DEC_BUCKETS) - 1;
-        return ng;
+        const DecodeSplit sp = decode_split(c + 1);
+        bucket = min(sp.per_wave / 32, DEC_BUCKETS) - 1;  // 32-token steps per wave
+        return sp.items;
     };
     // Pass 1: count decode items per bucket; list the prefill items.
     for (int base = 0; base < num_seqs; base += PLAN_THREADS) {
@@ -449,16 +446,13 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
     const int lr = lane / CPR;  // K loads: row of this lane in one instruction
     const int lc = lane % CPR;  // loads: 16-byte chunk of this lane (dims 8 lc .. 8 lc + 7)
     const int vr = (A < 32 ? (lane & 15) : lane) / CPR;  // V loads: 4-row group
-    // Workgroup -> (work item, kv head, head chunk).  Workgroups go to the 8
-    // XCDs round-robin by linear id, each XCD with its own L2; the head
-    // chunks of one (item, kv head) are 8 ids apart, so they run on one XCD
-    // at about the same time and all but the first find the K/V rows in its
-    // L2.  The grid covers the capacity (rounded up to 8 pairs for chunks);
-    // workgroups past the planned count leave at once.
+    // Workgroup -> (work item, kv head, head chunk) by decode_unit: the head
+    // chunks of one (item, kv head) pair run on one XCD, 8 launch ids apart.
+    // The grid covers the capacity; workgroups past the planned count leave
+    // at once.
     const int64_t n_pairs = (int64_t)P.hdr[HDR_N_DEC] * P.hkv;
-    const int64_t lid = blockIdx.x;
-    const int64_t pair = P.HC == 1 ? lid : (lid >> 3) / P.HC * 8 + (lid & 7);
-    if (pair >= n_pairs) return;  // the whole workgroup
+    const DecodeUnit unit = decode_unit(blockIdx.x, P.HC);
+    if (unit.pair >= n_pairs) return;  // the whole workgroup
     if (threadIdx.x == 0) arrived = 0;
     __syncthreads();  // the only barrier: waves past the sequence leave below
     uint4* vt = &sVt[wave][0];
@@ -468,19 +462,21 @@ __global__ __launch_bounds__(256, NG == 2 && A <= 128 ? 2 : 1) void decode_mfma_
     }
 
     const int GW = P.G / P.HC;  // heads of this wave (<= 16 * NG)
-    const int hc = P.HC == 1 ? 0 : (int)((lid >> 3) % P.HC);
-    const int kvh = pair % P.hkv;
-    const int item = pair / P.hkv;
+    const int hc = unit.hc;
+    const int kvh = unit.pair % P.hkv;
+    const int item = unit.pair / P.hkv;
     const int2 it = P.items[item];
     const int s = it.x;
     const int L = P.ctx[s] + 1;
     const int row = P.cu[s];
-    // The sequence's items split it evenly: each covers span tokens (the
-    // last one fewer) and each wave a quarter of that, a multiple of STEP
-    // tokens and at most one partition.  Item count and split depend only on
-    // the sequence's own length.
-    const int ngroups = (L + GP * DP - 1) / (GP * DP);  // work items of the sequence
-    const int per_wave = ((L + GP * ngroups - 1) / (GP * ngroups) + STEP - 1) / STEP * STEP;
+    // The sequence's items split it evenly (decode_split): each covers span
+    // tokens (the last one fewer) and each wave a quarter of that, a
+    // multiple of STEP tokens and at most one partition.  Item count and
+    // split depend only on the sequence's own length.
+    static_assert(STEP == 32 && DP == DECODE_PART && GP == DECODE_GROUP, "decode_split's shares");
+    const DecodeSplit split = decode_split(L);
+    const int ngroups = split.items;  // work items of the sequence
+    const int per_wave = split.per_wave;
     const int span = GP * per_wave;
     const int i0 = it.y * span;
     const int t0 = i0 + wave * per_wave;
@@ -1062,11 +1058,8 @@ hipError_t launch_decode(const StepArgs& a) {
     p.G = G;
     p.HC = G / GW;
     p.scale_log2 = a.scale * 1.4426950408889634f;
-    const int64_t units = a.lay.cap_dec * a.num_kv_heads * p.HC;
-    // one workgroup per unit, the head chunks of one (item, kv head) 8 launch
-    // ids apart (so the pairs are padded to a multiple of 8)
-    const int64_t pairs8 = (a.lay.cap_dec * a.num_kv_heads + 7) / 8 * 8;
-    const int64_t grid64 = p.HC == 1 ? units : pairs8 * p.HC;
+    // one workgroup per decode unit (decode_unit / decode_grid)
+    const int64_t grid64 = decode_grid(a.lay.cap_dec * a.num_kv_heads, p.HC);
     if (grid64 <= 0) return hipSuccess;
     if (grid64 > INT32_MAX) return hipErrorInvalidValue;
     const int grid = (int)grid64;

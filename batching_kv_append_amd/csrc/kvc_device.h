@@ -94,6 +94,41 @@ inline int prefill_span(int G, int nw = 4) { return PREFILL_QW * (nw / prefill_h
 // exist per item.
 constexpr int DECODE_GROUP = 4;  // partitions per decode workgroup (its four waves)
 
+// Split of a decode sequence of L keys (cached + the new one): `items` work
+// items of equal length, each cut into DECODE_GROUP wave shares of
+// `per_wave` keys (a multiple of 32, at most DECODE_PART), so wave w of item
+// i covers keys [(i G + w) per_wave, min(L, (i G + w + 1) per_wave)) and
+// waves starting at or past L have none.  It depends on L alone, so a
+// sequence's partial sums never depend on the rest of the batch; the planner
+// and the decode kernel both take it from here.
+struct DecodeSplit {
+    int items, per_wave;
+};
+__host__ __device__ inline DecodeSplit decode_split(int L) {
+    const int items = (L + DECODE_GROUP * DECODE_PART - 1) / (DECODE_GROUP * DECODE_PART);
+    const int share = (L + DECODE_GROUP * items - 1) / (DECODE_GROUP * items);
+    return {items, (share + 31) / 32 * 32};
+}
+
+// Launch id -> decode unit: the (work item x kv head) pair and the head
+// chunk.  The hardware deals launch ids to the 8 XCDs round-robin, each XCD
+// with its own L2; with HC > 1 head chunks the chunks of one pair get ids 8
+// apart, so they run on one XCD at about the same time and all but the
+// first find the pair's K/V rows in its L2.  decode_grid is the launch size
+// for `pairs` pairs (rounded up to 8 pairs when HC > 1); ids whose pair is
+// at or past `pairs` have no unit.
+struct DecodeUnit {
+    int64_t pair;
+    int hc;
+};
+__host__ __device__ inline DecodeUnit decode_unit(int64_t lid, int HC) {
+    if (HC == 1) return {lid, 0};
+    return {(lid >> 3) / HC * 8 + (lid & 7), (int)((lid >> 3) % HC)};
+}
+__host__ __device__ inline int64_t decode_grid(int64_t pairs, int HC) {
+    return HC == 1 ? pairs : (pairs + 7) / 8 * 8 * HC;
+}
+
 inline WsLayout ws_layout(int32_t num_seqs, int32_t total_q, int32_t max_context_len,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
     WsLayout w{};

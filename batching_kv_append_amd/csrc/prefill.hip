@@ -71,31 +71,18 @@ struct PrefillParams {
     const PreItem* items;
     int64_t num_blocks;
     int32_t max_blocks, hq, hkv, G, HC;
-    int32_t xcd_map;   // 1: head slots % 8 == 0, 2: 8 % head slots == 0, 0: plain
     float scale_log2;  // scale * log2(e)
 };
 
 // Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
 // linear id.  The grid is one-dimensional over (work item, head slot), head
-// slot = kv head x head chunk, laid out so that one XCD serves a fixed set of
-// head slots: the K/V of a kv head are then fetched into one L2 (or, with
-// fewer than 8 slots, into 8 / slots of them) instead of all eight.  Within
-// an XCD, items keep the planner's costliest-first order.
-__device__ __forceinline__ void prefill_unit(int L, int slots, int mode, int& item, int& slot) {
-    const int xcd = L & 7, r = L >> 3;
-    if (mode == 1) {
-        const int per = slots >> 3;
-        slot = (r % per) * 8 + xcd;
-        item = r / per;
-    } else if (mode == 2) {
-        const int groups = 8 / slots;
-        slot = xcd % slots;
-        item = r * groups + xcd / slots;
-    } else {
-        slot = L % slots;
-        item = L / slots;
-    }
-}
+// slot = kv head x head chunk, item-major: workgroup L is item L / slots,
+// slot L % slots, so it runs on XCD (item x slots + slot) mod 8.  With a
+// slot count that is a multiple of 8 that is slot mod 8, and with one that
+// divides 8 the XCD fixes the slot (XCD mod slots): either way an XCD serves
+// a fixed set of head slots, and the K/V of a kv head are fetched into one L2
+// (or, with fewer than 8 slots, into 8 / slots of them) instead of all
+// eight.  Within an XCD, items keep the planner's costliest-first order.
 
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -172,8 +159,8 @@ __global__ __launch_bounds__(64 * NW, A > 128 ? 1 : 2) void prefill_kernel(Prefi
     const int hi = lane >> 5;   // which half of the wave
     const int col = lane & 31;  // query column of this lane
 
-    int item, slot;
-    prefill_unit((int)blockIdx.x, P.hkv * P.HC, P.xcd_map, item, slot);
+    const int slots = P.hkv * P.HC;
+    const int item = (int)blockIdx.x / slots, slot = (int)blockIdx.x % slots;
     // The item's record (sequence, lengths) is read together with the
     // planned count: item is below the list's capacity, so the read is in
     // bounds either way, and testing both values keeps the two loads in one
@@ -578,7 +565,6 @@ hipError_t launch_prefill(const StepArgs& a) {
     p.HC = G / hpw;
     p.scale_log2 = a.scale * 1.4426950408889634f;
     const int slots = a.num_kv_heads * p.HC;
-    p.xcd_map = (slots % 8 == 0) ? 1 : (8 % slots == 0) ? 2 : 0;
     const int64_t gx = a.lay.cap_pre * slots;
     if (gx <= 0) return hipSuccess;
     if (gx > INT32_MAX) return hipErrorInvalidValue;

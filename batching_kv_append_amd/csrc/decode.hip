@@ -29,6 +29,8 @@
 // first.
 #include <hip/hip_runtime.h>
 
+#include <hip/hip_ext.h>
+
 #include "kvc_launch.h"
 
 namespace kvc {
@@ -1000,7 +1002,7 @@ int decode_heads_per_wave(int G, int head_dim, int block_size) {
     return 1;
 }
 
-hipError_t launch_prep(const StepArgs& a, bool with_append) {
+hipError_t launch_prep(const StepArgs& a, bool with_append, hipEvent_t done) {
     char* ws = a.ws;
     const int G = a.num_q_heads / a.num_kv_heads;
     PrepParams p;
@@ -1030,7 +1032,11 @@ hipError_t launch_prep(const StepArgs& a, bool with_append) {
     p.block_size = a.block_size;
     const int64_t rows_per_wg = PLAN_THREADS / 64;
     const int64_t grid = 1 + (with_append ? ((int64_t)a.total_q + rows_per_wg - 1) / rows_per_wg : 0);
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(PLAN_THREADS), 0, a.stream, p);
+    if (done)  // the launch itself records `done` when the kernel completes
+        hipExtLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(PLAN_THREADS), 0, a.stream, nullptr,
+                              done, 0, p);
+    else
+        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(PLAN_THREADS), 0, a.stream, p);
     return hipGetLastError();
 }
 

@@ -49,7 +49,8 @@ hipError_t launch_gather(const void* k_cache, const void* v_cache, int64_t num_b
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks,
                               const int32_t* src, const int32_t* dst, int32_t n, int32_t hkv,
                               int32_t head_dim, int32_t block_size, hipStream_t stream);
-hipError_t launch_prep(const StepArgs& a, bool with_append);
+// done (optional): an event that the planning kernel's own completion records
+hipError_t launch_prep(const StepArgs& a, bool with_append, hipEvent_t done = nullptr);
 // Split-K decode partials (+ direct output for one-partition sequences).
 hipError_t launch_decode(const StepArgs& a);
 // Log-sum-exp merge of the partials of multi-partition decode sequences.
